@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: large CPU work (oracle at full sizes)")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _oracle_built():
+    # the oracle is test infrastructure: make sure its shared object exists
+    from oracle.build import build_oracle
+
+    build_oracle(force=False)
+    yield
