@@ -1,0 +1,217 @@
+"""Python binding of libfa.so, the gfx950 exact-attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/fa.h.  The functions named like
+the C entry points (fa_fwd, fa_fwd_ex, fa_bwd, fa_bwd_workspace_bytes,
+fa_fwd_blocksparse, fa_status_str) take torch device tensors, read their
+shapes and pointers and call the C function of the same name on the current
+torch stream (or the stream given).  fwd, bwd and fwd_blocksparse are the same
+calls with the outputs (and the backward workspace) allocated by torch.
+
+There is no fallback: importing this package raises if libfa.so has not been
+built, and every call raises FAError on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads torch's HIP runtime first, so libfa.so binds to the same one
+
+__all__ = [
+    "FAError", "fa_status_str", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_bytes",
+    "fa_fwd_blocksparse", "fwd", "bwd", "fwd_blocksparse", "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libfa.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        f"{library_path} is missing: build it first (python -m exact_io_aware_36_amd.build)")
+
+_lib = ctypes.CDLL(library_path)
+
+
+def _check_single_hip_runtime():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        return
+    if len(paths) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(paths)}); import torch first")
+
+
+_check_single_hip_runtime()
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_lib.fa_status_str.restype = ctypes.c_char_p
+_lib.fa_status_str.argtypes = [_i]
+_lib.fa_fwd.restype = _i
+_lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp]
+_lib.fa_fwd_ex.restype = _i
+_lib.fa_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _i, _vp]
+_lib.fa_bwd_workspace_bytes.restype = _sz
+_lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
+_lib.fa_bwd.restype = _i
+_lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                        _vp, _i, _vp, _sz, _vp]
+_lib.fa_fwd_blocksparse.restype = _i
+_lib.fa_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _i, _vp]
+
+FA_DTYPE_BF16 = 0
+FA_DTYPE_FP32 = 1
+_DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_FP32}
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_str(status)}")
+
+
+def fa_status_str(status: int) -> str:
+    return _lib.fa_status_str(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream):
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _shape(q: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def _dtype(q: torch.Tensor) -> int:
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return _DTYPES[q.dtype]
+
+
+def _require(ok: bool, msg: str):
+    if not ok:
+        raise ValueError(msg)
+
+
+def _same(q, *ts):
+    for t in ts:
+        _require(t.shape == q.shape and t.dtype == q.dtype and t.device == q.device,
+                 "tensors must share shape, dtype and device")
+        _require(t.is_contiguous(), "tensors must be contiguous")
+    _require(q.is_contiguous(), "tensors must be contiguous")
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _check_rc(rc: int, where: str):
+    if rc != 0:
+        raise FAError(rc, where)
+
+
+def fa_fwd_ex(q, k, v, o, lse, causal=False, scale=None, kv_lens=None, tile_n=0, stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, o)
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * N,
+             "lse must be contiguous fp32 [B, H, N]")
+    if kv_lens is not None:
+        _require(kv_lens.dtype == torch.int32 and kv_lens.numel() == B, "kv_lens must be int32 [B]")
+    rc = _lib.fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                        _scale(scale, d), _ptr(kv_lens), _dtype(q), int(tile_n), _stream(q, stream))
+    _check_rc(rc, "fa_fwd_ex")
+
+
+def fa_fwd(q, k, v, o, lse, causal=False, scale=None, kv_lens=None, stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, o)
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * N,
+             "lse must be contiguous fp32 [B, H, N]")
+    if kv_lens is not None:
+        _require(kv_lens.dtype == torch.int32 and kv_lens.numel() == B, "kv_lens must be int32 [B]")
+    rc = _lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                     _scale(scale, d), _ptr(kv_lens), _dtype(q), _stream(q, stream))
+    _check_rc(rc, "fa_fwd")
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal=False, scale=None, kv_lens=None,
+           stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, o, dout, dq, dk, dv)
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * N,
+             "lse must be contiguous fp32 [B, H, N]")
+    if kv_lens is not None:
+        _require(kv_lens.dtype == torch.int32 and kv_lens.numel() == B, "kv_lens must be int32 [B]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = _lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                     _ptr(dv), B, H, N, d, int(bool(causal)), _scale(scale, d), _ptr(kv_lens),
+                     _dtype(q), _ptr(workspace), ws_bytes, _stream(q, stream))
+    _check_rc(rc, "fa_bwd")
+
+
+def fa_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_block=128, scale=None, stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, o)
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * N,
+             "lse must be contiguous fp32 [B, H, N]")
+    _require(block_mask.dtype == torch.uint8 and block_mask.is_contiguous(),
+             "block_mask must be contiguous uint8")
+    nb = N // mask_block if mask_block > 0 else 0
+    _require(block_mask.numel() == nb * nb, "block_mask must be [N/mask_block, N/mask_block]")
+    rc = _lib.fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                 _scale(scale, d), _ptr(block_mask), int(mask_block), _dtype(q),
+                                 _stream(q, stream))
+    _check_rc(rc, "fa_fwd_blocksparse")
+
+
+# -- the same calls with torch-allocated outputs ------------------------------
+
+def fwd(q, k, v, causal=False, scale=None, kv_lens=None, tile_n=0, stream=None):
+    """Return (O, LSE)."""
+    B, H, N, d = _shape(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_ex(q, k, v, o, lse, causal=causal, scale=scale, kv_lens=kv_lens, tile_n=tile_n,
+              stream=stream)
+    return o, lse
+
+
+def bwd(q, k, v, o, dout, lse, causal=False, scale=None, kv_lens=None, stream=None):
+    """Return (dQ, dK, dV)."""
+    B, H, N, d = _shape(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal=causal, scale=scale, kv_lens=kv_lens,
+           stream=stream)
+    return dq, dk, dv
+
+
+def fwd_blocksparse(q, k, v, block_mask, mask_block=128, scale=None, stream=None):
+    """Return (O, LSE)."""
+    B, H, N, d = _shape(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_block=mask_block, scale=scale,
+                       stream=stream)
+    return o, lse

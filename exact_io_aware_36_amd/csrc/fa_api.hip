@@ -1,0 +1,132 @@
+// fa_api.hip -- the C ABI of libfa.so: argument checks, kernel choice and
+// launch.  Every entry point only enqueues on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+fa_status check_common(const void *q, const void *k, const void *v, int B, int H, int N, int d,
+                       float scale)
+{
+    if (!q || !k || !v)
+        return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1)
+        return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale))
+        return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * N * d >= ((int64_t)1 << 31))
+        return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+} // namespace
+
+extern "C" {
+
+const char *fa_status_str(fa_status s)
+{
+    switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int H, int N, int d, int causal, float scale, const int32_t *kv_lens,
+                    fa_dtype dtype, int tile_n, fa_stream_t stream)
+{
+    fa_status st = check_common(q, k, v, B, H, N, d, scale);
+    if (st != FA_OK)
+        return st;
+    if (!o || !lse || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_INVALID_ARG;
+    if (kv_lens && !aligned(kv_lens, 4))
+        return FA_ERR_INVALID_ARG;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale, kv_lens, nullptr, 0};
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == FA_DTYPE_BF16) {
+        if (tile_n != 0 && tile_n != 64 && tile_n != 128)
+            return FA_ERR_UNSUPPORTED;
+        return from_hip(fa::launch_fwd_bf16(a, d, tile_n, causal != 0, false, s));
+    }
+    if (dtype == FA_DTYPE_FP32) {
+        if (tile_n != 0 && tile_n != 32)
+            return FA_ERR_UNSUPPORTED;
+        return from_hip(fa::launch_fwd_f32(a, d, causal != 0, s));
+    }
+    return FA_ERR_UNSUPPORTED;
+}
+
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                 int N, int d, int causal, float scale, const int32_t *kv_lens, fa_dtype dtype,
+                 fa_stream_t stream)
+{
+    return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, causal, scale, kv_lens, dtype, 0, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d)
+{
+    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128))
+        return 0;
+    const size_t bytes = (size_t)B * H * N * sizeof(float);
+    return (bytes + 255) / 256 * 256;
+}
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+                 int causal, float scale, const int32_t *kv_lens, fa_dtype dtype,
+                 void *workspace, size_t workspace_bytes, fa_stream_t stream)
+{
+    fa_status st = check_common(q, k, v, B, H, N, d, scale);
+    if (st != FA_OK)
+        return st;
+    if (!o || !dout || !lse || !dq || !dk || !dv)
+        return FA_ERR_INVALID_ARG;
+    if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16) || !aligned(lse, 4) || (kv_lens && !aligned(kv_lens, 4)))
+        return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return FA_ERR_WORKSPACE;
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, H, N, scale, kv_lens};
+    return from_hip(fa::launch_bwd_bf16(a, d, causal != 0, (hipStream_t)stream));
+}
+
+fa_status fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int B, int H, int N, int d, float scale, const uint8_t *block_mask,
+                             int mask_block, fa_dtype dtype, fa_stream_t stream)
+{
+    fa_status st = check_common(q, k, v, B, H, N, d, scale);
+    if (st != FA_OK)
+        return st;
+    if (!o || !lse || !block_mask || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_INVALID_ARG;
+    if (mask_block != 128 || N % mask_block != 0)
+        return FA_ERR_INVALID_ARG;
+    if (N / mask_block > 512)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale, nullptr, block_mask, N / mask_block};
+    return from_hip(fa::launch_fwd_bf16(a, d, 0, false, true, (hipStream_t)stream));
+}
+
+} // extern "C"

@@ -1,0 +1,465 @@
+// fa_fwd.hip -- forward attention kernels for gfx950 (CDNA4).
+//
+// Exact attention O = softmax(scale Q K^T) V computed tile by tile with the
+// running-statistics recurrence ("The Attention Matrix You Never Write Down",
+// section "The running-statistics trick", steps 1-4; "FlashAttention:
+// Mathematical Foundations, IO-Aware Tiling, Online Softmax, and Recomputation
+// Dynamics", sections "Incremental Online Updates" and "IO-Aware Tiling
+// Algorithm").  Per query row the kernel keeps the running maximum m, the
+// running sum l and an unnormalised output accumulator; a new key tile with a
+// larger maximum rescales l and the accumulator by exp(m - m'), and the
+// accumulator is divided by l once at the end.  Only O and the row's
+// log-sum-exp are written.
+//
+// Schedule.  One workgroup of 4 wave64s owns 128 query rows of one (b, h) and
+// streams every key/value tile through LDS (queries outer, keys inner: the
+// work partitioning of the same article's "FlashAttention-2" section, rather
+// than the key-outer loop of its Algorithm 1, so O, m and l never leave
+// registers).  Each wave owns 32 query rows.
+//
+// Data layout on chip.  The score tile is computed transposed, S^T = K Q^T,
+// with v_mfma_f32_32x32x16_bf16: the MFMA result gives each lane one query
+// column and 16 key rows, so the row max and row sum of a query are a
+// reduction over the lane's own registers plus one exchange with the lane 32
+// away.  The probabilities then feed O^T += V^T P^T directly as the B operand
+// (same lane = same query, same key order), so P never touches LDS.  K sits
+// in LDS row-major; V sits in LDS transposed (d-major) so that the A operand
+// of the second product is two 8-byte reads per lane.
+//
+// Exponentials use exp2 with the scale folded in: t = S * scale * log2(e),
+// P = 2^(t - m) with m tracked in log2 units, and LSE = ln2 * (m + log2 l).
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr int MAX_MASK_BLOCKS = 512;   // sparse: N <= 65536 with 128-blocks
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 forward.  D = head dim, BC = keys per tile, BR = 128 queries per
+// workgroup.  SPARSE walks the nonzero 128-blocks of the workgroup's mask row.
+template <int D, int BC, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log2)
+{
+    constexpr int BR = 128;
+    constexpr int KSTEPS = D / 16;         // k-steps of S^T over d
+    constexpr int NKC = BC / 32;           // 32-key chunks per tile
+    constexpr int NDB = D / 32;            // 32-wide d blocks of O^T
+    constexpr int KS = D + 8;              // LDS row stride of K (bf16)
+    constexpr int VS = BC + 4;             // LDS row stride of V^T (bf16)
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int CH = BC * CPR / 256;     // chunks per thread per tile
+    static_assert(CH * 256 == BC * CPR, "tile must split evenly over 256 threads");
+
+    __shared__ __attribute__((aligned(16))) bf16 ks[2][BC * KS];
+    __shared__ __attribute__((aligned(16))) bf16 vt[2][D * VS];
+    __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
+    __shared__ int bcount;
+
+    const int N = p.N;
+    const int n_qblk = (N + BR - 1) / BR;
+    const int total = p.B * p.H * n_qblk;
+    const int w = xcd_remap(blockIdx.x, total);
+    const int bh = w / n_qblk;
+    int qb = w % n_qblk;
+    if (CAUSAL)
+        qb = n_qblk - 1 - qb;                // longest rows first
+    const int b = bh / p.H;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int q0 = qb * BR;
+    const int wq0 = q0 + wave * 32;          // first query of this wave
+    const int qrow = wq0 + l32;              // this lane's query
+
+    const size_t head_off = (size_t)bh * N * D;
+    const bf16 *Q = (const bf16 *)p.q + head_off;
+    const bf16 *K = (const bf16 *)p.k + head_off;
+    const bf16 *V = (const bf16 *)p.v + head_off;
+
+    int kv_len = N;
+    if (p.kv_lens) {
+        kv_len = p.kv_lens[b];
+        kv_len = kv_len < 0 ? 0 : (kv_len > N ? N : kv_len);
+    }
+
+    // ---- the tiles this workgroup visits
+    int n_tiles;
+    constexpr int TPB = 128 / BC;            // tiles per 128-block (sparse)
+    if constexpr (SPARSE) {
+        if (wave == 0) {
+            const uint8_t *mrow = p.mask + (size_t)qb * p.nb;
+            int cnt = 0;
+            for (int base = 0; base < p.nb; base += 64) {
+                const int c = base + lane;
+                const bool on = c < p.nb && mrow[c] != 0;
+                const unsigned long long bits = __ballot(on);
+                const int pos = cnt + __popcll(bits & ((1ull << lane) - 1ull));
+                if (on)
+                    blist[pos] = c;
+                cnt += __popcll(bits);
+            }
+            if (lane == 0)
+                bcount = cnt;
+        }
+        __syncthreads();
+        n_tiles = bcount * TPB;
+    } else {
+        int kv_end = kv_len;
+        if (CAUSAL)
+            kv_end = min(kv_end, q0 + BR);
+        n_tiles = (kv_end + BC - 1) / BC;
+    }
+    auto tile_of = [&](int t) -> int {
+        if constexpr (SPARSE)
+            return blist[t / TPB] * TPB + t % TPB;
+        else
+            return t;
+    };
+
+    // ---- Q as the B operand of S^T = K Q^T: lane holds its query's d-slice
+    bf16x8 qreg[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        if (qrow < N)
+            qreg[s] = *(const bf16x8 *)(Q + (size_t)qrow * D + s * 16 + hf * 8);
+        else
+            qreg[s] = bf16x8{};
+    }
+
+    // ---- cooperative tile staging through registers
+    bf16x8 kreg[CH], vreg[CH];
+    auto load_tile = [&](int j) {
+#pragma unroll
+        for (int r = 0; r < CH; ++r) {
+            const int cidx = tid + 256 * r;
+            const int row = cidx / CPR, col = (cidx % CPR) * 8;
+            const int key = j * BC + row;
+            if (key < N) {
+                kreg[r] = *(const bf16x8 *)(K + (size_t)key * D + col);
+                vreg[r] = *(const bf16x8 *)(V + (size_t)key * D + col);
+            } else {
+                kreg[r] = bf16x8{};
+                vreg[r] = bf16x8{};
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < CH; ++r) {
+            const int cidx = tid + 256 * r;
+            const int row = cidx / CPR, col = (cidx % CPR) * 8;
+            *(bf16x8 *)&ks[buf][row * KS + col] = kreg[r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vt[buf][(col + e) * VS + row] = vreg[r][e];
+        }
+    };
+
+    float m = -INFINITY;   // running max (log2 units), same in both lane halves
+    float lsum = 0.f;      // running sum, partial over this lane half's keys
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        oacc[db] = f32x16{};
+
+    if (n_tiles > 0) {
+        load_tile(tile_of(0));
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const int buf = t & 1;
+        const int j = tile_of(t);
+        if (t + 1 < n_tiles)
+            load_tile(tile_of(t + 1));
+
+        const int kbase = j * BC;
+        // whole tile above this wave's diagonal: nothing to add
+        const bool skip = CAUSAL && kbase > wq0 + 31;
+        if (!skip) {
+            // S^T = K_j Q^T
+            f32x16 s[NKC];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                s[kc] = f32x16{};
+                const bf16 *krow = &ks[buf][(kc * 32 + l32) * KS + hf * 8];
+#pragma unroll
+                for (int st = 0; st < KSTEPS; ++st)
+                    s[kc] = mfma_bf16(*(const bf16x8 *)(krow + st * 16), qreg[st], s[kc]);
+            }
+            // masks: only tiles that cross the diagonal or the key length
+            const bool need_mask = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
+            if (need_mask) {
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kbase + kc * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
+                        if (key >= kv_len || (CAUSAL && key > qrow))
+                            s[kc][i] = -INFINITY;
+                    }
+            }
+            // running max
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, s[kc][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m, mx * c_log2);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m - m_use);
+            m = m_new;
+            // probabilities, row sum, bf16 operands for P V
+            float rs = 0.f;
+            bf16x8 pb[NKC][2];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float pv = fast_exp2(fmaf(s[kc][i], c_log2, -m_use));
+                    rs += pv;
+                    pb[kc][i / 8][i % 8] = (bf16)pv;
+                }
+            lsum = alpha * lsum + rs;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                oacc[db] *= alpha;
+            // O^T += V_j^T P^T
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const bf16 *vrow = &vt[buf][(db * 32 + l32) * VS + 4 * hf];
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const bf16 *src = vrow + kc * 32 + hh * 16;
+                        const bf16x4 a0 = *(const bf16x4 *)src;
+                        const bf16x4 a1 = *(const bf16x4 *)(src + 8);
+                        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        oacc[db] = mfma_bf16(a, pb[kc][hh], oacc[db]);
+                    }
+            }
+        }
+        if (t + 1 < n_tiles)
+            store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = acc / l, LSE = ln2 (m + log2 l)
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (qrow < N) {
+        bf16 *O = (bf16 *)p.o + head_off + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ov[e] = (bf16)(oacc[db][4 * g + e] * inv);
+                *(bf16x4 *)(O + db * 32 + 8 * g + 4 * hf) = ov;
+            }
+        if (hf == 0)
+            p.lse[(size_t)bh * N + qrow] = ltot > 0.f ? LN2 * (m + __log2f(ltot)) : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 forward (full-precision operands through v_mfma_f32_32x32x2_f32).
+// Same transposed schedule; 32 keys per tile; one LDS buffer.  With one
+// element of k per lane the V operand is a plain row-major read.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p, float c_log2)
+{
+    constexpr int BR = 128, BC = 32;
+    constexpr int KSTEPS = D / 2;
+    constexpr int NDB = D / 32;
+    constexpr int KS = D + 1;   // K row stride (floats)
+    constexpr int VS = D + 4;   // V row stride (floats)
+    __shared__ float ks[BC * KS];
+    __shared__ float vs[BC * VS];
+
+    const int N = p.N;
+    const int n_qblk = (N + BR - 1) / BR;
+    const int total = p.B * p.H * n_qblk;
+    const int w = xcd_remap(blockIdx.x, total);
+    const int bh = w / n_qblk;
+    int qb = w % n_qblk;
+    if (CAUSAL)
+        qb = n_qblk - 1 - qb;
+    const int b = bh / p.H;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int q0 = qb * BR;
+    const int wq0 = q0 + wave * 32;
+    const int qrow = wq0 + l32;
+    const size_t head_off = (size_t)bh * N * D;
+    const float *Q = (const float *)p.q + head_off;
+    const float *K = (const float *)p.k + head_off;
+    const float *V = (const float *)p.v + head_off;
+
+    int kv_len = N;
+    if (p.kv_lens) {
+        kv_len = p.kv_lens[b];
+        kv_len = kv_len < 0 ? 0 : (kv_len > N ? N : kv_len);
+    }
+    int kv_end = kv_len;
+    if (CAUSAL)
+        kv_end = min(kv_end, q0 + BR);
+    const int n_tiles = (kv_end + BC - 1) / BC;
+
+    float qreg[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+        qreg[s] = qrow < N ? Q[(size_t)qrow * D + 2 * s + hf] : 0.f;
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        oacc[db] = f32x16{};
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const int kbase = t * BC;
+        for (int idx = tid; idx < BC * D; idx += 256) {
+            const int row = idx / D, col = idx % D;
+            const int key = kbase + row;
+            ks[row * KS + col] = key < N ? K[(size_t)key * D + col] : 0.f;
+            vs[row * VS + col] = key < N ? V[(size_t)key * D + col] : 0.f;
+        }
+        __syncthreads();
+        const bool skip = CAUSAL && kbase > wq0 + 31;
+        if (!skip) {
+            f32x16 s = f32x16{};
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st)
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[l32 * KS + 2 * st + hf], qreg[st], s, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = kbase + 8 * (i / 4) + 4 * hf + (i % 4);
+                if (key >= kv_len || (CAUSAL && key > qrow))
+                    s[i] = -INFINITY;
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                mx = fmaxf(mx, s[i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m, mx * c_log2);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m - m_use);
+            m = m_new;
+            float rs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[i] = fast_exp2(fmaf(s[i], c_log2, -m_use));
+                rs += s[i];
+            }
+            lsum = alpha * lsum + rs;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                oacc[db] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = 8 * (i / 4) + 4 * hf + (i % 4);
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * VS + db * 32 + l32], s[i],
+                                                                   oacc[db], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (qrow < N) {
+        float *O = (float *)p.o + head_off + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                O[db * 32 + 8 * (i / 4) + 4 * hf + (i % 4)] = oacc[db][i] * inv;
+        if (hf == 0)
+            p.lse[(size_t)bh * N + qrow] = ltot > 0.f ? LN2 * (m + __log2f(ltot)) : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int BC, bool CAUSAL, bool SPARSE>
+static hipError_t launch_bf16_inst(const FwdArgs &a, hipStream_t s)
+{
+    const int n_qblk = (a.N + 127) / 128;
+    const dim3 grid(a.B * a.H * n_qblk), block(256);
+    FwdArgs args = a;
+    float c = a.scale * LOG2E;
+    void *kargs[] = {&args, &c};
+    return hipLaunchKernel((const void *)&fwd_bf16_kernel<D, BC, CAUSAL, SPARSE>, grid, block,
+                           kargs, 0, s);
+}
+
+template <int D, int BC>
+static hipError_t launch_bf16_d_bc(const FwdArgs &a, bool causal, bool sparse, hipStream_t s)
+{
+    if (sparse)
+        return launch_bf16_inst<D, BC, false, true>(a, s);
+    return causal ? launch_bf16_inst<D, BC, true, false>(a, s)
+                  : launch_bf16_inst<D, BC, false, false>(a, s);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, int d, int tile_n, bool causal, bool sparse,
+                           hipStream_t s)
+{
+    if (tile_n == 0)
+        tile_n = 64;
+    if (d == 64 && tile_n == 64)
+        return launch_bf16_d_bc<64, 64>(a, causal, sparse, s);
+    if (d == 64 && tile_n == 128)
+        return launch_bf16_d_bc<64, 128>(a, causal, sparse, s);
+    if (d == 128 && tile_n == 64)
+        return launch_bf16_d_bc<128, 64>(a, causal, sparse, s);
+    if (d == 128 && tile_n == 128)
+        return launch_bf16_d_bc<128, 128>(a, causal, sparse, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal, hipStream_t s)
+{
+    const int n_qblk = (a.N + 127) / 128;
+    const dim3 grid(a.B * a.H * n_qblk), block(256);
+    FwdArgs args = a;
+    float c = a.scale * LOG2E;
+    void *kargs[] = {&args, &c};
+    const void *fn;
+    if (d == 64)
+        fn = causal ? (const void *)&fwd_f32_kernel<64, true> : (const void *)&fwd_f32_kernel<64, false>;
+    else if (d == 128)
+        fn = causal ? (const void *)&fwd_f32_kernel<128, true> : (const void *)&fwd_f32_kernel<128, false>;
+    else
+        return hipErrorInvalidValue;
+    return hipLaunchKernel(fn, grid, block, kargs, 0, s);
+}
+
+} // namespace fa

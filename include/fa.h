@@ -1,0 +1,158 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library libfa.so.
+ *
+ * The library computes exact scaled dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * tile by tile with an online softmax, so the N x N score and probability
+ * matrices never reach device memory ("FlashAttention: Mathematical
+ * Foundations, IO-Aware Tiling, Online Softmax, and Recomputation Dynamics",
+ * sections "The GPU Memory Hierarchy and the Attention Memory Wall" and
+ * "IO-Aware Tiling Algorithm"; "The Attention Matrix You Never Write Down",
+ * section "The running-statistics trick").  The forward pass stores only O and
+ * one per-row statistic, the log-sum-exp; the backward pass recomputes the
+ * score and probability tiles on chip from Q, K, V and that statistic (same
+ * article, section "Backward Pass and Activation Recomputation").  A
+ * block-sparse forward skips the tiles a block mask zeroes ("Attention",
+ * learn-kernels.com, paragraph on block-sparse FlashAttention).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Layout: Q, K, V, O, dO, dQ, dK, dV are dense [B][H][N][d] tensors with d
+ *    innermost (row stride d elements, no padding).  LSE is dense fp32
+ *    [B][H][N].
+ *  - LSE is the natural-log log-sum-exp of the row's scaled scores over the
+ *    allowed keys: LSE_i = ln(sum_j exp(scale * q_i . k_j)).  A row with no
+ *    allowed key gets LSE = -inf and O = 0.
+ *  - Masks: causal allows key j for query i iff j <= i.  kv_lens (nullable)
+ *    is a device int32[B]; key j of batch entry b is allowed iff
+ *    j < kv_lens[b]; every query row is still computed and written.  A block
+ *    mask excludes the keys of a zero block from the softmax entirely.
+ *  - Pointers: every tensor pointer is a DEVICE pointer owned by the caller;
+ *    outputs must not alias inputs.  The library allocates nothing, keeps no
+ *    mutable global state and is re-entrant.
+ *  - Streams: every call only enqueues work on `stream` (NULL = the default
+ *    stream) and returns without synchronising; results are valid once the
+ *    stream has reached that point.  Calls on different streams that share
+ *    output buffers race.
+ *  - Errors: return codes only.  Arguments are checked on the host before
+ *    anything is enqueued; nothing is launched when a check fails.  The
+ *    contents of device buffers (kv_lens values, mask bytes) are not checked:
+ *    kv_lens values outside [0, N] are undefined behaviour.
+ *  - Supported: d in {64, 128}; dtype BF16 everywhere; dtype FP32 for the
+ *    dense forward only.  bf16 tensors are IEEE bfloat16, rounded to nearest
+ *    even on store; all accumulation is fp32.
+ *  - Sizes: B, H, N >= 1 and B*H*N*d < 2^31.
+ *  - Alignment: tensor pointers 16-byte aligned, LSE and kv_lens 4-byte
+ *    aligned, the backward workspace 256-byte aligned (FA_ERR_INVALID_ARG,
+ *    resp. FA_ERR_WORKSPACE, otherwise).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t, declared here so that the header needs no
+ * HIP include. */
+struct ihipStream_t;
+typedef struct ihipStream_t *fa_stream_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad scale, bad mask block */
+    FA_ERR_UNSUPPORTED = 2, /* d, dtype or tile not built */
+    FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    FA_ERR_LAUNCH = 4       /* the HIP runtime refused the launch */
+} fa_status;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *fa_status_str(fa_status s);
+
+/*
+ * Forward: O and LSE from Q, K, V.
+ *   q, k, v   in  [B][H][N][d], dtype
+ *   o         out [B][H][N][d], dtype
+ *   lse       out [B][H][N] fp32 (natural log)
+ *   causal    0 or 1
+ *   scale     finite, > 0 (normally 1/sqrt(d))
+ *   kv_lens   nullable device int32[B] key-padding lengths
+ * Errors: FA_ERR_INVALID_ARG for a null q/k/v/o/lse, B/H/N < 1, a
+ * non-finite or non-positive scale, or B*H*N*d >= 2^31; FA_ERR_UNSUPPORTED
+ * for d not in {64, 128} or an unknown dtype.
+ */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int H, int N, int d, int causal, float scale,
+                 const int32_t *kv_lens, fa_dtype dtype, fa_stream_t stream);
+
+/*
+ * fa_fwd with an explicit key/value tile length tile_n (the B_c of the
+ * pages' block-size constraint B_r*d + 2*B_c*d <= M, "FlashAttention:
+ * Mathematical Foundations ...", section "IO-Aware Tiling Algorithm").
+ * tile_n = 0 picks the default (64 for bf16, 32 for fp32); 64 and 128 are
+ * built for bf16 and 32 for fp32.  Other values give FA_ERR_UNSUPPORTED.
+ * Results equal fa_fwd's up to rounding order.
+ */
+fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int N, int d, int causal, float scale,
+                    const int32_t *kv_lens, fa_dtype dtype, int tile_n,
+                    fa_stream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (the per-row
+ * D_i = dO_i . O_i of the backward, fp32 [B][H][N], rounded up to 256 B).
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward: dQ, dK, dV of L = sum(O * dO) from Q, K, V, O, dO and the LSE
+ * the forward stored; S and P are recomputed tile by tile ("FlashAttention:
+ * Mathematical Foundations ...", section "Backward Pass and Activation
+ * Recomputation").  The gradient formulas are the chain rule of the
+ * definition: dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i,
+ * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ *   q, k, v, o, dout  in  [B][H][N][d] bf16
+ *   lse               in  [B][H][N] fp32, as written by fa_fwd with the same
+ *                         q, k, v, causal, scale and kv_lens
+ *   dq, dk, dv        out [B][H][N][d] bf16 (dK, dV rows of padded keys are 0)
+ *   workspace         device scratch of at least fa_bwd_workspace_bytes()
+ *                     bytes, 256-byte aligned; contents on entry ignored
+ * Errors: as fa_fwd, plus FA_ERR_WORKSPACE when workspace is NULL or
+ * workspace_bytes is too small, and FA_ERR_UNSUPPORTED for dtype FP32.
+ */
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
+                 const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                 int B, int H, int N, int d, int causal, float scale,
+                 const int32_t *kv_lens, fa_dtype dtype, void *workspace,
+                 size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * Block-sparse forward ("Attention", learn-kernels.com, paragraph on
+ * block-sparse FlashAttention): like fa_fwd (non-causal, no padding), but
+ * the keys of block (r, c) are visible to the queries of block r only when
+ * block_mask[r * (N / mask_block) + c] != 0.  Zero blocks are skipped, not
+ * computed.
+ *   block_mask  device uint8 [N/mask_block][N/mask_block], row-major,
+ *               shared by every (b, h)
+ *   mask_block  must be 128; N must be a multiple of it and N <= 65536
+ * A query row whose mask row is all zero gets O = 0, LSE = -inf.
+ * Errors: as fa_fwd, plus FA_ERR_INVALID_ARG for a null mask, a mask_block
+ * other than 128 or N % mask_block != 0; FA_ERR_UNSUPPORTED for dtype FP32
+ * or N > 65536.
+ */
+fa_status fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *o,
+                             float *lse, int B, int H, int N, int d, float scale,
+                             const uint8_t *block_mask, int mask_block, fa_dtype dtype,
+                             fa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

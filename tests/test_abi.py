@@ -1,0 +1,145 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host with the documented
+status codes.  Every call below fails a host-side check, so nothing is ever
+launched (the fake pointers are never dereferenced)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH = 0, 1, 2, 3, 4
+BF16, FP32 = 0, 1
+P = 0x10000        # a 256-byte-aligned fake device address, never dereferenced
+MIS = 0x10008      # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    fa = pytest.importorskip("exact_io_aware_36_amd")
+    return fa._lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_bytes",
+                 "fa_fwd_blocksparse", "fa_status_str"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import exact_io_aware_36_amd as fa
+
+    raw = ctypes.CDLL(fa.library_path)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+        # and the Python binding has a function of the same name
+        assert callable(getattr(fa, name)), name
+
+
+def test_status_strings(lib):
+    import exact_io_aware_36_amd as fa
+
+    assert fa.fa_status_str(OK) == "FA_OK"
+    assert fa.fa_status_str(INVALID) == "FA_ERR_INVALID_ARG"
+    assert fa.fa_status_str(UNSUPPORTED) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_str(WORKSPACE) == "FA_ERR_WORKSPACE"
+    assert fa.fa_status_str(LAUNCH) == "FA_ERR_LAUNCH"
+    assert fa.fa_status_str(99) == "FA_ERR_UNKNOWN"
+
+
+def test_workspace_bytes(lib):
+    assert lib.fa_bwd_workspace_bytes(1, 16, 16384, 128) == 16 * 16384 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256          # rounded up
+    assert lib.fa_bwd_workspace_bytes(16, 16, 512, 64) == 16 * 16 * 512 * 4
+    assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1, 96) == 0
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, scale=0.125,
+        lens=None, dtype=BF16, tile=None):
+    if tile is None:
+        return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, lens, dtype, None)
+    return lib.fa_fwd_ex(q, k, v, o, lse, B, H, N, d, causal, scale, lens, dtype, tile, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(o=None), INVALID), (dict(lse=None), INVALID),
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=0), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(B=1 << 14, H=16, N=1 << 14, d=64), INVALID),      # B*H*N*d >= 2^31
+    (dict(q=MIS), INVALID), (dict(o=MIS), INVALID), (dict(lse=P + 2), INVALID),
+    (dict(lens=P + 1), INVALID),
+])
+def test_fwd_rejects(lib, kw, want):
+    assert fwd(lib, **kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(tile=32), UNSUPPORTED), (dict(tile=256), UNSUPPORTED), (dict(tile=-1), UNSUPPORTED),
+    (dict(tile=64, dtype=FP32), UNSUPPORTED), (dict(tile=16, dtype=FP32), UNSUPPORTED),
+    (dict(tile=64, d=80), UNSUPPORTED), (dict(tile=64, q=None), INVALID),
+])
+def test_fwd_ex_rejects(lib, kw, want):
+    assert fwd(lib, **kw) == want
+
+
+def bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=2, N=256, d=64, causal=0,
+        scale=0.125, lens=None, dtype=BF16, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    return lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, causal, scale, lens, dtype,
+                      ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(do=None), INVALID),
+    (dict(lse=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
+    (dict(dv=None), INVALID), (dict(N=0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(dtype=FP32), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+    (dict(ws=P + 16), WORKSPACE), (dict(dq=MIS), INVALID),
+])
+def test_bwd_rejects(lib, kw, want):
+    assert bwd(lib, **kw) == want
+
+
+def sparse(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=256, d=64, scale=0.125, mask=P,
+           mb=128, dtype=BF16):
+    return lib.fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, mask, mb, dtype, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(mask=None), INVALID), (dict(mb=64), INVALID), (dict(mb=0), INVALID),
+    (dict(N=200), INVALID), (dict(N=131072), UNSUPPORTED), (dict(dtype=FP32), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED), (dict(o=None), INVALID), (dict(scale=-0.5), INVALID),
+])
+def test_sparse_rejects(lib, kw, want):
+    assert sparse(lib, **kw) == want
+
+
+def test_python_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    fa = pytest.importorskip("exact_io_aware_36_amd")
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, torch.zeros(1, 1, 9, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.fwd(q.view(8, 64), q.view(8, 64), q.view(8, 64))
+    with pytest.raises(ValueError):
+        fa.fwd(q.half(), q.half(), q.half())
