@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input: the
+forward kernel and the three backward launches (D = rowsum(dO * O), the
+keys-outer dK/dV kernel, the queries-outer dQ kernel), each through the C ABI
+on torch's current stream.  Default workload: long-context causal attention,
+B=1, H=16, N=16384, d=128, bf16 (inputs N(0,1) * 0.5, dO N(0,1)).
+
+FLOP convention: forward = 4 N^2 d B H, halved when causal, times the
+nonzero-block fraction when block-sparse; forward + backward = 2.5 x forward.
+value = (flops of one step) / (wall time of one step), in TFLOP/s.
+
+The JSON line also carries
+  roofline: the dominant kernel (largest average launch time, measured with
+            HIP events on the launch stream over the timed steps): its
+            algorithmic flops per launch / its average duration, against the
+            bf16 dense MFMA peak of 2.5 PFLOP/s; traffic is the HBM bytes per
+            launch from the committed rocprofv3 counter summary when it was
+            taken on the current kernel source, else null;
+  cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
+            random sample of query rows of the same workload (forward rows
+            plus the backward dQ of those rows), scaled to TFLOP/s with the
+            same convention.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+
+# kernel name (as rocprofv3 reports it) -> source file, for the traffic
+# summaries' staleness check
+KERNEL_SOURCES = {
+    "fwd": "exact_io_aware_36_amd/csrc/fa_fwd.hip",
+    "bwd_dot": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
+    "bwd_dkdv": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
+    "bwd_dq": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
+}
+
+
+# ---------------------------------------------------------------------------
+# accounting (no attention arithmetic: counts only)
+
+def fwd_flops(B, H, N, d, causal=False, sparse_frac=None) -> float:
+    f = 4.0 * N * N * d * B * H
+    if causal:
+        f *= 0.5
+    if sparse_frac is not None:
+        f *= sparse_frac
+    return f
+
+
+def step_flops(B, H, N, d, causal=False, sparse_frac=None, backward=False) -> float:
+    f = fwd_flops(B, H, N, d, causal, sparse_frac)
+    return 2.5 * f if backward else f
+
+
+def kernel_flops(stage, B, H, N, d, causal=False, sparse_frac=None) -> float:
+    """Algorithmic matrix-product flops one launch performs: the forward does
+    two products per (query, allowed key) pair (S and P V), the dK/dV kernel
+    four (S, dP, dV, dK), the dQ kernel three (S, dP, dQ); 2 d flops each."""
+    f = fwd_flops(B, H, N, d, causal, sparse_frac)
+    return {"fwd": f, "bwd_dkdv": 2.0 * f, "bwd_dq": 1.5 * f, "bwd_dot": 0.0}[stage]
+
+
+def floor_bytes(stage, B, H, N, d, elem=2) -> float:
+    """The O(N d) input/output floor of one launch."""
+    t = B * H * N * d * elem
+    rows = B * H * N * 4
+    return {
+        "fwd": 4 * t + rows,                 # Q, K, V in; O out; LSE out
+        "bwd_dot": 2 * t + rows,             # O, dO in; D out
+        "bwd_dkdv": 6 * t + 2 * rows,        # Q, K, V, dO, LSE, D in; dK, dV out
+        "bwd_dq": 5 * t + 2 * rows,          # Q, K, V, dO, LSE, D in; dQ out
+    }[stage]
+
+
+def standard_io_elements(N, d) -> float:
+    """Standard attention's HBM traffic in elements, 2N^2 + 4Nd, as the
+    worked accounting of "01 · FlashAttention" (step 5 of 5, "show the
+    accounting") counts it."""
+    return 2.0 * N * N + 4.0 * N * d
+
+
+def flash_io_elements(N, d, M) -> float:
+    """The same page's tiled count, 4Nd + 2 N^2 d^2 / M, with M the number
+    of elements that fit on chip."""
+    return 4.0 * N * d + 2.0 * N * N * d * d / M
+
+
+# ---------------------------------------------------------------------------
+
+def source_digest(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(stage: str, workload: str):
+    """HBM bytes per launch from profiles/traffic_<stage>_<workload>.txt, or
+    None when absent or taken on another version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_digest(KERNEL_SOURCES[stage]):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, w, metric_flops, budget_s=15.0, seed=99):
+    """Time the oracle on a random sample of query rows (forward rows, and for
+    workloads with a backward also dQ of the same rows); credit the sample
+    with its share of the step's metric flops."""
+    import numpy as np
+
+    import oracle
+
+    B, H, N, d = inp["B"], inp["H"], inp["N"], inp["d"]
+    total_rows = B * H * N
+    f64 = {n: inp[n].double().numpy() for n in ("q", "k", "v") if inp.get(n) is not None}
+    if w.backward:
+        f64["dout"] = inp["dout"].double().numpy()
+    lens = inp["kv_lens"].numpy() if inp.get("kv_lens") is not None else None
+    mask = inp["block_mask"].numpy() if inp.get("block_mask") is not None else None
+    rng = np.random.default_rng(seed)
+
+    def run(rows):
+        oracle.fwd_rows(f64["q"], f64["k"], f64["v"], rows, causal=w.causal, scale=w.scale,
+                        kv_lens=lens, block_mask=mask, mask_block=w.mask_block)
+        if w.backward:
+            # dQ of the sampled rows, head by head
+            bh = rows // N
+            for g in np.unique(bh):
+                b, h = divmod(int(g), H)
+                sel = rows[bh == g] % N
+                oracle.bwd_sample(f64["q"][b, h], f64["k"][b, h], f64["v"][b, h],
+                                  f64["dout"][b, h], sel, np.zeros(0, np.int64), causal=w.causal,
+                                  scale=w.scale, kv_len=None if lens is None else int(lens[b]),
+                                  block_mask=mask, mask_block=w.mask_block)
+
+    probe = np.sort(rng.choice(total_rows, min(64, total_rows), replace=False))
+    t0 = time.perf_counter()
+    run(probe)
+    t_probe = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(total_rows, max(64, len(probe) * budget_s / t_probe)))
+    rows = np.sort(rng.choice(total_rows, n, replace=False))
+    t0 = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t0
+    flops = metric_flops * n / total_rows
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+        "sample": (f"{n} of {total_rows} query rows drawn uniformly at random: oracle fp64 forward "
+                   f"rows{' + backward dQ rows' if w.backward else ''}, {dt:.1f} s; credited "
+                   f"{n}/{total_rows} of one step's {metric_flops:.4g} flops"),
+        "seconds": dt,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_context_causal")
+    ap.add_argument("--tile", type=int, default=0, help="forward key tile (0 = default)")
+    ap.add_argument("--tile-sweep", default="64,128",
+                    help="forward key tiles to time on the side ('' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(heads and batch shard across GPUs with no communication; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_io_aware_36_amd as fa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    w = workloads.WORKLOADS[args.workload]
+    inp = workloads.make_inputs(w)
+    B, H, N, d = inp["B"], inp["H"], inp["N"], inp["d"]
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    dout = inp["dout"].to(dev) if w.backward else None
+    lens = inp["kv_lens"].to(dev) if inp["kv_lens"] is not None else None
+    mask = inp["block_mask"].to(dev) if inp["block_mask"] is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if w.backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    stages = ["fwd"] + (["bwd_dot", "bwd_dkdv", "bwd_dq"] if w.backward else [])
+
+    def launch(stage, tile=args.tile):
+        if stage == "fwd":
+            if mask is not None:
+                fa.fa_fwd_blocksparse(q, k, v, o, lse, mask, mask_block=w.mask_block, scale=w.scale)
+            else:
+                fa.fa_fwd_ex(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=lens,
+                             tile_n=tile)
+        elif stage == "bwd_dot":
+            fa.fa_bwd_preprocess(o, dout, ws)
+        elif stage == "bwd_dkdv":
+            fa.fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, ws, causal=w.causal, scale=w.scale,
+                           kv_lens=lens)
+        elif stage == "bwd_dq":
+            fa.fa_bwd_dq(q, k, v, dout, lse, dq, ws, causal=w.causal, scale=w.scale, kv_lens=lens)
+
+    for _ in range(args.warmup):
+        for s in stages:
+            launch(s)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        for j, s in enumerate(stages):
+            launch(s)
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    stage_ms = {s: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j, s in enumerate(stages)}
+
+    sf = w.sparse_frac
+    flops = step_flops(B, H, N, d, w.causal, sf, w.backward)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    dom = max(stages, key=lambda s: stage_ms[s])
+    dom_flops = kernel_flops(dom, B, H, N, d, w.causal, sf)
+    achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    traffic = read_traffic(dom, w.name)
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "avg_launch_ms": round(stage_ms[dom], 4)}
+
+    fflops = fwd_flops(B, H, N, d, w.causal, sf)
+    detail = {
+        "stage_ms": {s: round(t, 4) for s, t in stage_ms.items()},
+        "fwd_tflops": round(fflops / (stage_ms["fwd"] * 1e-3) / 1e12, 2),
+        "kernel_tflops": {s: round(kernel_flops(s, B, H, N, d, w.causal, sf) / (stage_ms[s] * 1e-3) / 1e12, 2)
+                          for s in stages if s != "bwd_dot"},
+        "floor_bytes_per_step": sum(floor_bytes(s, B, H, N, d) for s in stages),
+    }
+    if w.backward:
+        bwd_ms = sum(stage_ms[s] for s in stages if s != "fwd")
+        detail["bwd_tflops_1.5x"] = round(1.5 * fflops / (bwd_ms * 1e-3) / 1e12, 2)
+        detail["fwd_bwd_tflops_3.5x"] = round(3.5 * fflops / (ms_per_step * 1e-3) / 1e12, 2)
+
+    sweep = [int(t) for t in args.tile_sweep.split(",") if t.strip()] if mask is None else []
+    if sweep:
+        res = {}
+        for t in sweep:
+            for _ in range(3):
+                launch("fwd", tile=t)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(3, args.steps // 2)
+            e0.record(stream)
+            for _ in range(reps):
+                launch("fwd", tile=t)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res[str(t)] = {"fwd_ms": round(ms, 4), "fwd_tflops": round(fflops / (ms * 1e-3) / 1e12, 2)}
+        detail["fwd_tile_sweep"] = res
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, w, flops, budget_s=args.cpu_budget)
+        cpu = {k2: (round(v2, 6) if isinstance(v2, float) else v2) for k2, v2 in cpu.items()}
+
+    line = {
+        "metric": "attention TFLOP/s fwd & fwd+bwd, % bf16 MFMA peak, N=256-16K, d=64/128",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "pass": "fwd+bwd" if w.backward else "fwd",
+                   "flops_per_step": flops, "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+                   "flop_convention": "fwd 4N^2dBH (x1/2 causal, x s sparse); fwd+bwd 2.5x fwd"},
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/fa.h.  The functions named like
 the C entry points (fa_fwd, fa_fwd_ex, fa_bwd, fa_bwd_workspace_bytes,
-fa_fwd_blocksparse, fa_status_str) take torch device tensors, read their
+fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_fwd_blocksparse, fa_status_str) take torch device tensors, read their
 shapes and pointers and call the C function of the same name on the current
 torch stream (or the stream given).  fwd, bwd and fwd_blocksparse are the same
 calls with the outputs (and the backward workspace) allocated by torch.
@@ -21,7 +21,8 @@ import torch  # loads torch's HIP runtime first, so libfa.so binds to the same o
 
 __all__ = [
     "FAError", "fa_status_str", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_bytes",
-    "fa_fwd_blocksparse", "fwd", "bwd", "fwd_blocksparse", "library_path",
+    "fa_fwd_blocksparse", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fwd", "bwd",
+    "fwd_blocksparse", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,6 +66,14 @@ _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
 _lib.fa_bwd.restype = _i
 _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                         _vp, _i, _vp, _sz, _vp]
+_lib.fa_bwd_preprocess.restype = _i
+_lib.fa_bwd_preprocess.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+_lib.fa_bwd_dkdv.restype = _i
+_lib.fa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i,
+                             _vp, _sz, _vp]
+_lib.fa_bwd_dq.restype = _i
+_lib.fa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz,
+                           _vp]
 _lib.fa_fwd_blocksparse.restype = _i
 _lib.fa_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _i, _vp]
 
@@ -168,6 +177,38 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal=False, scale=Non
                      _ptr(dv), B, H, N, d, int(bool(causal)), _scale(scale, d), _ptr(kv_lens),
                      _dtype(q), _ptr(workspace), ws_bytes, _stream(q, stream))
     _check_rc(rc, "fa_bwd")
+
+
+def _ws_bytes(workspace):
+    return workspace.numel() * workspace.element_size() if workspace is not None else 0
+
+
+def fa_bwd_preprocess(o, dout, workspace, stream=None):
+    B, H, N, d = _shape(o)
+    _same(o, dout)
+    rc = _lib.fa_bwd_preprocess(_ptr(o), _ptr(dout), B, H, N, d, _dtype(o), _ptr(workspace),
+                                _ws_bytes(workspace), _stream(o, stream))
+    _check_rc(rc, "fa_bwd_preprocess")
+
+
+def fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, causal=False, scale=None, kv_lens=None,
+                stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, dout, dk, dv)
+    rc = _lib.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dk), _ptr(dv), B, H,
+                          N, d, int(bool(causal)), _scale(scale, d), _ptr(kv_lens), _dtype(q),
+                          _ptr(workspace), _ws_bytes(workspace), _stream(q, stream))
+    _check_rc(rc, "fa_bwd_dkdv")
+
+
+def fa_bwd_dq(q, k, v, dout, lse, dq, workspace, causal=False, scale=None, kv_lens=None,
+              stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, dout, dq)
+    rc = _lib.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq), B, H, N, d,
+                        int(bool(causal)), _scale(scale, d), _ptr(kv_lens), _dtype(q),
+                        _ptr(workspace), _ws_bytes(workspace), _stream(q, stream))
+    _check_rc(rc, "fa_bwd_dq")
 
 
 def fa_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_block=128, scale=None, stream=None):

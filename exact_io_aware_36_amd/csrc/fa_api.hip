@@ -88,10 +88,13 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d)
     return (bytes + 255) / 256 * 256;
 }
 
-fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                 const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
-                 int causal, float scale, const int32_t *kv_lens, fa_dtype dtype,
-                 void *workspace, size_t workspace_bytes, fa_stream_t stream)
+// Shared checks of fa_bwd and its stages.  A stage that does not use one of
+// the tensors passes one it does use in its place.
+static fa_status check_bwd(const void *q, const void *k, const void *v, const void *o,
+                           const void *dout, const float *lse, const void *dq, const void *dk,
+                           const void *dv, int B, int H, int N, int d, float scale,
+                           const int32_t *kv_lens, fa_dtype dtype, const void *workspace,
+                           size_t workspace_bytes)
 {
     fa_status st = check_common(q, k, v, B, H, N, d, scale);
     if (st != FA_OK)
@@ -106,8 +109,62 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
     const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return FA_ERR_WORKSPACE;
+    return FA_OK;
+}
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+                 int causal, float scale, const int32_t *kv_lens, fa_dtype dtype,
+                 void *workspace, size_t workspace_bytes, fa_stream_t stream)
+{
+    fa_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, kv_lens, dtype,
+                             workspace, workspace_bytes);
+    if (st != FA_OK)
+        return st;
     fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, H, N, scale, kv_lens};
     return from_hip(fa::launch_bwd_bf16(a, d, causal != 0, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_preprocess(const void *o, const void *dout, int B, int H, int N, int d,
+                            fa_dtype dtype, void *workspace, size_t workspace_bytes,
+                            fa_stream_t stream)
+{
+    // o and dout stand in for every other tensor pointer of the full check
+    fa_status st = check_bwd(o, o, o, o, dout, (const float *)workspace, o, o, o, B, H, N, d, 1.f,
+                             nullptr, dtype, workspace, workspace_bytes);
+    if (st != FA_OK)
+        return st;
+    fa::BwdArgs a{nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr,
+                  (float *)workspace, B, H, N, 1.f, nullptr};
+    return from_hip(fa::launch_bwd_stage(a, d, false, fa::BwdStage::Dot, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
+                      const float *lse, void *dk, void *dv, int B, int H, int N, int d,
+                      int causal, float scale, const int32_t *kv_lens, fa_dtype dtype,
+                      const void *workspace, size_t workspace_bytes, fa_stream_t stream)
+{
+    fa_status st = check_bwd(q, k, v, dout, dout, lse, dk, dk, dv, B, H, N, d, scale, kv_lens,
+                             dtype, workspace, workspace_bytes);
+    if (st != FA_OK)
+        return st;
+    fa::BwdArgs a{q, k, v, nullptr, dout, lse, nullptr, dk, dv, (float *)workspace, B, H, N, scale,
+                  kv_lens};
+    return from_hip(fa::launch_bwd_stage(a, d, causal != 0, fa::BwdStage::DkDv, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
+                    const float *lse, void *dq, int B, int H, int N, int d, int causal,
+                    float scale, const int32_t *kv_lens, fa_dtype dtype, const void *workspace,
+                    size_t workspace_bytes, fa_stream_t stream)
+{
+    fa_status st = check_bwd(q, k, v, dout, dout, lse, dq, dq, dq, B, H, N, d, scale, kv_lens,
+                             dtype, workspace, workspace_bytes);
+    if (st != FA_OK)
+        return st;
+    fa::BwdArgs a{q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, (float *)workspace, B, H, N,
+                  scale, kv_lens};
+    return from_hip(fa::launch_bwd_stage(a, d, causal != 0, fa::BwdStage::Dq, (hipStream_t)stream));
 }
 
 fa_status fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -413,37 +413,69 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
     }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_bwd_inst(const BwdArgs &a, hipStream_t s)
+template <int D>
+hipError_t launch_dot(const BwdArgs &a, hipStream_t s)
 {
     const int rows = a.B * a.H * a.N;
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL(bwd_dot_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s,
-                       (const bf16 *)a.o, (const bf16 *)a.dout, a.dvec, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
+    const bf16 *o = (const bf16 *)a.o, *g = (const bf16 *)a.dout;
+    float *dvec = a.dvec;
+    void *kargs[] = {&o, &g, &dvec, (void *)&rows};
+    return hipLaunchKernel((const void *)&bwd_dot_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256),
+                           kargs, 0, s);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv(const BwdArgs &a, hipStream_t s)
+{
     BwdArgs args = a;
     float c = a.scale * LOG2E_B;
     void *kargs[] = {&args, &c};
     const int n_kb = (a.N + 127) / 128;
-    e = hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, CAUSAL>, dim3(a.B * a.H * n_kb), dim3(256),
-                        kargs, 0, s);
-    if (e != hipSuccess)
-        return e;
-    return hipLaunchKernel((const void *)&bwd_dq_kernel<D, CAUSAL>, dim3(a.B * a.H * n_kb), dim3(256),
-                           kargs, 0, s);
+    return hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, CAUSAL>, dim3(a.B * a.H * n_kb),
+                           dim3(256), kargs, 0, s);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq(const BwdArgs &a, hipStream_t s)
+{
+    BwdArgs args = a;
+    float c = a.scale * LOG2E_B;
+    void *kargs[] = {&args, &c};
+    const int n_qb = (a.N + 127) / 128;
+    return hipLaunchKernel((const void *)&bwd_dq_kernel<D, CAUSAL>, dim3(a.B * a.H * n_qb),
+                           dim3(256), kargs, 0, s);
 }
 
 } // namespace
 
+hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, BwdStage stage, hipStream_t s)
+{
+    if (d != 64 && d != 128)
+        return hipErrorInvalidValue;
+    switch (stage) {
+    case BwdStage::Dot:
+        return d == 64 ? launch_dot<64>(a, s) : launch_dot<128>(a, s);
+    case BwdStage::DkDv:
+        if (d == 64)
+            return causal ? launch_dkdv<64, true>(a, s) : launch_dkdv<64, false>(a, s);
+        return causal ? launch_dkdv<128, true>(a, s) : launch_dkdv<128, false>(a, s);
+    case BwdStage::Dq:
+        if (d == 64)
+            return causal ? launch_dq<64, true>(a, s) : launch_dq<64, false>(a, s);
+        return causal ? launch_dq<128, true>(a, s) : launch_dq<128, false>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, hipStream_t s)
 {
-    if (d == 64)
-        return causal ? launch_bwd_inst<64, true>(a, s) : launch_bwd_inst<64, false>(a, s);
-    if (d == 128)
-        return causal ? launch_bwd_inst<128, true>(a, s) : launch_bwd_inst<128, false>(a, s);
-    return hipErrorInvalidValue;
+    hipError_t e = launch_bwd_stage(a, d, causal, BwdStage::Dot, s);
+    if (e == hipSuccess)
+        e = launch_bwd_stage(a, d, causal, BwdStage::DkDv, s);
+    if (e == hipSuccess)
+        e = launch_bwd_stage(a, d, causal, BwdStage::Dq, s);
+    return e;
 }
 
 } // namespace fa

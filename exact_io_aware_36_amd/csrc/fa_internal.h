@@ -34,6 +34,8 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, int tile_n, bool causal, boo
                            hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, hipStream_t s);
+enum class BwdStage { Dot, DkDv, Dq };
+hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, BwdStage stage, hipStream_t s);
 
 // The workgroup-to-tile remap used by every attention grid: workgroups are
 // dispatched round-robin over the 8 XCDs, so work item w is given to the

@@ -133,6 +133,30 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
                  size_t workspace_bytes, fa_stream_t stream);
 
 /*
+ * The three launches fa_bwd makes, callable one by one on the same stream
+ * and in this order (results equal fa_bwd's bit for bit).  Useful to time
+ * or overlap the stages separately.  Arguments mean what they mean for
+ * fa_bwd; the workspace must be the same buffer for all three calls.
+ *   fa_bwd_preprocess: workspace <- D_i = dO_i . O_i (fp32 [B][H][N]).
+ *   fa_bwd_dkdv:       dK, dV from Q, K, V, dO, LSE and the workspace
+ *                      (keys-outer kernel).
+ *   fa_bwd_dq:         dQ from Q, K, V, dO, LSE and the workspace
+ *                      (queries-outer kernel).
+ * Errors: as fa_bwd.
+ */
+fa_status fa_bwd_preprocess(const void *o, const void *dout, int B, int H, int N, int d,
+                            fa_dtype dtype, void *workspace, size_t workspace_bytes,
+                            fa_stream_t stream);
+fa_status fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
+                      const float *lse, void *dk, void *dv, int B, int H, int N, int d,
+                      int causal, float scale, const int32_t *kv_lens, fa_dtype dtype,
+                      const void *workspace, size_t workspace_bytes, fa_stream_t stream);
+fa_status fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
+                    const float *lse, void *dq, int B, int H, int N, int d, int causal,
+                    float scale, const int32_t *kv_lens, fa_dtype dtype, const void *workspace,
+                    size_t workspace_bytes, fa_stream_t stream);
+
+/*
  * Block-sparse forward ("Attention", learn-kernels.com, paragraph on
  * block-sparse FlashAttention): like fa_fwd (non-causal, no padding), but
  * the keys of block (r, c) are visible to the queries of block r only when

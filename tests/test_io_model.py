@@ -1,0 +1,70 @@
+"""The benchmark's accounting against the worked IO example printed by
+"01 · FlashAttention" (step 5 of 5 "The payoff", panel "show the accounting"),
+stored in tests/golden/io_accounting_n8192_d128_m65536.txt with its citation,
+and the flop convention against closed forms."""
+from __future__ import annotations
+
+import os
+
+import pytest
+
+import bench
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "io_accounting_n8192_d128_m65536.txt")
+
+
+def load_golden():
+    vals = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split()
+                vals[k] = float(v)
+    return vals
+
+
+def test_io_accounting_matches_the_page():
+    g = load_golden()
+    N, d, M = int(g["N"]), int(g["d"]), int(g["M"])
+    std = bench.standard_io_elements(N, d)
+    fl = bench.flash_io_elements(N, d, M)
+    assert N * N == g["score_entries_per_head"]
+    assert std == g["standard_elements"]
+    assert fl == g["flash_elements"]
+    assert round(std / fl, 1) == g["traffic_reduction"]
+    # the page's bars: 2-byte elements at 2 TB/s, 2 N^2 d flops at 312 TFLOP/s
+    wait_std = std * 2 / 2e12 * 1e6
+    wait_fl = fl * 2 / 2e12 * 1e6
+    compute = 2 * N * N * d / 312e12 * 1e6
+    assert round(wait_std) == g["standard_wait_us"]
+    assert round(wait_fl) == g["flash_wait_us"]
+    assert round(compute) == g["compute_us"]
+    assert round(wait_std + compute) == g["standard_total_us"]
+    assert round(wait_fl + compute) == g["flash_total_us"]
+    assert round((wait_std + compute) / (wait_fl + compute), 1) == g["speedup"]
+
+
+def test_flop_convention():
+    # forward: two products of 2 N^2 d flops per head
+    assert bench.fwd_flops(1, 1, 256, 64) == 4 * 256 * 256 * 64
+    assert bench.fwd_flops(8, 16, 1024, 64, causal=True) == 17179869184
+    assert bench.fwd_flops(1, 16, 16384, 128, causal=True) == 1099511627776
+    assert bench.fwd_flops(4, 16, 4096, 64, sparse_frac=0.25) == 68719476736
+    assert bench.step_flops(16, 16, 512, 64, backward=True) == 2.5 * 17179869184
+    # per-kernel products: dK/dV four, dQ three, forward two
+    f = bench.fwd_flops(1, 2, 512, 64, causal=True)
+    assert bench.kernel_flops("bwd_dkdv", 1, 2, 512, 64, causal=True) == 2 * f
+    assert bench.kernel_flops("bwd_dq", 1, 2, 512, 64, causal=True) == 1.5 * f
+
+
+def test_floor_bytes():
+    B, H, N, d = 1, 16, 16384, 128
+    assert bench.floor_bytes("fwd", B, H, N, d) == 269484032
+    t = B * H * N * d * 2
+    assert bench.floor_bytes("bwd_dkdv", B, H, N, d) == 6 * t + 8 * B * H * N
+
+
+def test_gpus_above_one_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
