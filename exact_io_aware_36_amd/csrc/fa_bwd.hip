@@ -25,42 +25,20 @@
 // MFMA layouts (v_mfma_f32_32x32x16_bf16).  In the key-outer kernel the
 // score tile is S (queries x keys), so each lane holds one key and 16 query
 // rows; P and dS then feed dV^T += dO^T P and dK^T += Q^T dS as B operands
-// without leaving registers, and the A operands dO^T, Q^T are read from
-// transposed copies in LDS.  In the query-outer kernel the tile is S^T, each
-// lane holds one query (so LSE_i and D_i are lane-local), and
-// dQ^T += K^T dS^T reads K^T from a transposed LDS copy.
+// without leaving registers, and the A operands dO^T, Q^T come from the
+// row-major Q and dO tiles through the hardware transpose read.  In the
+// query-outer kernel the tile is S^T, each lane holds one query (so LSE_i and
+// D_i are lane-local), and dQ^T += K^T dS^T reads K^T from the row-major K
+// tile the same way.  Tiles are swizzled and double-buffered (fa_tile.h).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include "fa_internal.h"
+#include "fa_tile.h"
 
 namespace fa {
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 namespace {
-
-constexpr float LOG2E_B = 1.4426950408889634f;
-
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ f32x16 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Two 4-element runs 8 apart, the k-order that pairs with an MFMA result's
-// register order (regs 4g..4g+3 of lane half h hold rows 8g + 4h + 0..3).
-__device__ __forceinline__ bf16x8 load_pair4(const bf16 *src)
-{
-    const bf16x4 a0 = *(const bf16x4 *)src;
-    const bf16x4 a1 = *(const bf16x4 *)(src + 8);
-    return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 // D_i = dO_i . O_i in fp32 -----------------------------------------------
 template <int D>
@@ -95,18 +73,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
     constexpr int KSTEPS = D / 16;
     constexpr int NQC = BQ / 32;           // 32-query chunks per tile
     constexpr int NDB = D / 32;
-    constexpr int RS = D + 8;              // row-major stride (bf16)
-    constexpr int TS = BQ + 4;             // transposed stride (bf16)
-    constexpr int CPR = D / 8;
-    constexpr int CH = BQ * CPR / 256;
-    static_assert(CH * 256 == BQ * CPR, "tile must split evenly");
 
-    __shared__ __attribute__((aligned(16))) bf16 qs[BQ * RS];
-    __shared__ __attribute__((aligned(16))) bf16 qt[D * TS];
-    __shared__ __attribute__((aligned(16))) bf16 dos[BQ * RS];
-    __shared__ __attribute__((aligned(16))) bf16 dot_[D * TS];
-    __shared__ __attribute__((aligned(16))) float lse_s[BQ];
-    __shared__ __attribute__((aligned(16))) float dd_s[BQ];
+    __shared__ __attribute__((aligned(16))) bf16 qs[2][BQ * D];
+    __shared__ __attribute__((aligned(16))) bf16 dos[2][BQ * D];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
+    __shared__ __attribute__((aligned(16))) float dd_s[2][BQ];
 
     const int N = p.N;
     const int n_kb = (N + BKV - 1) / BKV;
@@ -160,39 +131,43 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
     const int qt_end = (k0 < kv_len) ? n_qt : qt_begin;   // no allowed key: nothing to do
     const bool wave_live = wk0 < kv_len;
 
-    for (int it = qt_begin; it < qt_end; ++it) {
+    TileStage<BQ, D> qst, gst;
+    float lse_r = INFINITY, dd_r = 0.f;    // threads < BQ stage one row's LSE and D
+    auto load_tile = [&](int it) {
         const int qbase = it * BQ;
-        // stage Q, dO (row-major and transposed), LSE (log2 units), D
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-            const int cidx = tid + 256 * r;
-            const int row = cidx / CPR, col = (cidx % CPR) * 8;
-            const int qi = qbase + row;
-            bf16x8 qv{}, gv{};
-            if (qi < N) {
-                qv = *(const bf16x8 *)(Q + (size_t)qi * D + col);
-                gv = *(const bf16x8 *)(dO + (size_t)qi * D + col);
-            }
-            *(bf16x8 *)&qs[row * RS + col] = qv;
-            *(bf16x8 *)&dos[row * RS + col] = gv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qt[(col + e) * TS + row] = qv[e];
-                dot_[(col + e) * TS + row] = gv[e];
-            }
-        }
+        qst.load(Q + (size_t)qbase * D, N - qbase);
+        gst.load(dO + (size_t)qbase * D, N - qbase);
         if (tid < BQ) {
             const int qi = qbase + tid;
-            float l2 = INFINITY, dd = 0.f;   // rows past N: P = 0
+            lse_r = INFINITY;              // rows past N: P = 0
+            dd_r = 0.f;
             if (qi < N) {
                 const float l = LSE[qi];
-                l2 = (l == -INFINITY) ? INFINITY : l * LOG2E_B;
-                dd = Dv[qi];
+                lse_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
+                dd_r = Dv[qi];
             }
-            lse_s[tid] = l2;
-            dd_s[tid] = dd;
         }
-        __syncthreads();
+    };
+    auto store_tile = [&](int buf) {
+        qst.store(qs[buf]);
+        gst.store(dos[buf]);
+        if (tid < BQ) {
+            lse_s[buf][tid] = lse_r;
+            dd_s[buf][tid] = dd_r;
+        }
+    };
+
+    if (qt_begin < qt_end) {
+        load_tile(qt_begin);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int it = qt_begin; it < qt_end; ++it) {
+        const int buf = (it - qt_begin) & 1;
+        const int qbase = it * BQ;
+        if (it + 1 < qt_end)
+            load_tile(it + 1);
 
         const bool skip = !wave_live || (CAUSAL && qbase + BQ - 1 < wk0);
         if (!skip) {
@@ -201,12 +176,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
             for (int qc = 0; qc < NQC; ++qc) {
                 s[qc] = f32x16{};
                 dp[qc] = f32x16{};
-                const bf16 *qrow = &qs[(qc * 32 + l32) * RS + hf * 8];
-                const bf16 *grow = &dos[(qc * 32 + l32) * RS + hf * 8];
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st) {
-                    s[qc] = mfma16(*(const bf16x8 *)(qrow + st * 16), kreg[st], s[qc]);
-                    dp[qc] = mfma16(*(const bf16x8 *)(grow + st * 16), vreg[st], dp[qc]);
+                    s[qc] = mfma_bf16(ld_row8<D>(qs[buf], qc * 32 + l32, st * 16 + hf * 8), kreg[st], s[qc]);
+                    dp[qc] = mfma_bf16(ld_row8<D>(dos[buf], qc * 32 + l32, st * 16 + hf * 8), vreg[st], dp[qc]);
                 }
             }
             const bool need_mask = (CAUSAL && qbase < wk0 + 31) || (wk0 + 32 > kv_len);
@@ -216,8 +189,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int trow = qc * 32 + 8 * g + 4 * hf;
-                    const f32x4 l4 = *(const f32x4 *)&lse_s[trow];
-                    const f32x4 d4 = *(const f32x4 *)&dd_s[trow];
+                    const f32x4 l4 = *(const f32x4 *)&lse_s[buf][trow];
+                    const f32x4 d4 = *(const f32x4 *)&dd_s[buf][trow];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 4 * g + e;
@@ -230,18 +203,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
                     }
                 }
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16 *grow = &dot_[(db * 32 + l32) * TS + 4 * hf];
-                const bf16 *qrow = &qt[(db * 32 + l32) * TS + 4 * hf];
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int qc = 0; qc < NQC; ++qc)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        dv_acc[db] = mfma16(load_pair4(grow + qc * 32 + hh * 16), pb[qc][hh], dv_acc[db]);
-                        dk_acc[db] = mfma16(load_pair4(qrow + qc * 32 + hh * 16), dsb[qc][hh], dk_acc[db]);
+                        dv_acc[db] = mfma_bf16(ld_tr8<D>(dos[buf], qc * 32 + hh * 16, db * 32), pb[qc][hh], dv_acc[db]);
+                        dk_acc[db] = mfma_bf16(ld_tr8<D>(qs[buf], qc * 32 + hh * 16, db * 32), dsb[qc][hh], dk_acc[db]);
                     }
-            }
         }
+        if (it + 1 < qt_end)
+            store_tile(buf ^ 1);
         __syncthreads();
     }
 
@@ -273,15 +245,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
     constexpr int KSTEPS = D / 16;
     constexpr int NKC = BC / 32;
     constexpr int NDB = D / 32;
-    constexpr int RS = D + 8;
-    constexpr int TS = BC + 4;
-    constexpr int CPR = D / 8;
-    constexpr int CH = BC * CPR / 256;
-    static_assert(CH * 256 == BC * CPR, "tile must split evenly");
 
-    __shared__ __attribute__((aligned(16))) bf16 ks[BC * RS];
-    __shared__ __attribute__((aligned(16))) bf16 kt[D * TS];
-    __shared__ __attribute__((aligned(16))) bf16 vs[BC * RS];
+    __shared__ __attribute__((aligned(16))) bf16 ks[2][BC * D];
+    __shared__ __attribute__((aligned(16))) bf16 vs[2][BC * D];
 
     const int N = p.N;
     const int n_qblk = (N + BR - 1) / BR;
@@ -324,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
     float lse2 = INFINITY, dval = 0.f;
     if (qrow < N) {
         const float l = p.lse[(size_t)bh * N + qrow];
-        lse2 = (l == -INFINITY) ? INFINITY : l * LOG2E_B;
+        lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
         dval = p.dvec[(size_t)bh * N + qrow];
     }
 
@@ -338,25 +304,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
         kv_end = min(kv_end, q0 + BR);
     const int n_tiles = (kv_end + BC - 1) / BC;
 
+    TileStage<BC, D> kst, vst;
+    auto load_tile = [&](int t) {
+        const int key0 = t * BC;
+        kst.load(K + (size_t)key0 * D, N - key0);
+        vst.load(V + (size_t)key0 * D, N - key0);
+    };
+    if (n_tiles > 0) {
+        load_tile(0);
+        kst.store(ks[0]);
+        vst.store(vs[0]);
+    }
+    __syncthreads();
+
     for (int t = 0; t < n_tiles; ++t) {
+        const int buf = t & 1;
         const int kbase = t * BC;
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-            const int cidx = tid + 256 * r;
-            const int row = cidx / CPR, col = (cidx % CPR) * 8;
-            const int kj = kbase + row;
-            bf16x8 kv{}, vv{};
-            if (kj < N) {
-                kv = *(const bf16x8 *)(K + (size_t)kj * D + col);
-                vv = *(const bf16x8 *)(V + (size_t)kj * D + col);
-            }
-            *(bf16x8 *)&ks[row * RS + col] = kv;
-            *(bf16x8 *)&vs[row * RS + col] = vv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                kt[(col + e) * TS + row] = kv[e];
-        }
-        __syncthreads();
+        if (t + 1 < n_tiles)
+            load_tile(t + 1);
 
         const bool skip = CAUSAL && kbase > wq0 + 31;
         if (!skip) {
@@ -365,12 +330,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
             for (int kc = 0; kc < NKC; ++kc) {
                 s[kc] = f32x16{};
                 dp[kc] = f32x16{};
-                const bf16 *krow = &ks[(kc * 32 + l32) * RS + hf * 8];
-                const bf16 *vrow = &vs[(kc * 32 + l32) * RS + hf * 8];
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st) {
-                    s[kc] = mfma16(*(const bf16x8 *)(krow + st * 16), qreg[st], s[kc]);
-                    dp[kc] = mfma16(*(const bf16x8 *)(vrow + st * 16), greg[st], dp[kc]);
+                    s[kc] = mfma_bf16(ld_row8<D>(ks[buf], kc * 32 + l32, st * 16 + hf * 8), qreg[st], s[kc]);
+                    dp[kc] = mfma_bf16(ld_row8<D>(vs[buf], kc * 32 + l32, st * 16 + hf * 8), greg[st], dp[kc]);
                 }
             }
             const bool need_mask = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
@@ -386,14 +349,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
                     dsb[kc][i / 8][i % 8] = (bf16)(pv * (dp[kc][i] - dval));
                 }
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16 *krow = &kt[(db * 32 + l32) * TS + 4 * hf];
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh)
-                        dq_acc[db] = mfma16(load_pair4(krow + kc * 32 + hh * 16), dsb[kc][hh], dq_acc[db]);
-            }
+                        dq_acc[db] = mfma_bf16(ld_tr8<D>(ks[buf], kc * 32 + hh * 16, db * 32), dsb[kc][hh], dq_acc[db]);
+        }
+        if (t + 1 < n_tiles) {
+            kst.store(ks[buf ^ 1]);
+            vst.store(vs[buf ^ 1]);
         }
         __syncthreads();
     }
@@ -429,7 +394,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_dkdv(const BwdArgs &a, hipStream_t s)
 {
     BwdArgs args = a;
-    float c = a.scale * LOG2E_B;
+    float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     const int n_kb = (a.N + 127) / 128;
     return hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, CAUSAL>, dim3(a.B * a.H * n_kb),
@@ -440,7 +405,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_dq(const BwdArgs &a, hipStream_t s)
 {
     BwdArgs args = a;
-    float c = a.scale * LOG2E_B;
+    float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     const int n_qb = (a.N + 127) / 128;
     return hipLaunchKernel((const void *)&bwd_dq_kernel<D, CAUSAL>, dim3(a.B * a.H * n_qb),

@@ -22,34 +22,32 @@
 // column and 16 key rows, so the row max and row sum of a query are a
 // reduction over the lane's own registers plus one exchange with the lane 32
 // away.  The probabilities then feed O^T += V^T P^T directly as the B operand
-// (same lane = same query, same key order), so P never touches LDS.  K sits
-// in LDS row-major; V sits in LDS transposed (d-major) so that the A operand
-// of the second product is two 8-byte reads per lane.
+// (same lane = same query, same key order), so P never touches LDS.
 //
 // Exponentials use exp2 with the scale folded in: t = S * scale * log2(e),
 // P = 2^(t - m) with m tracked in log2 units, and LSE = ln2 * (m + log2 l).
+//
+// Lazy rescaling.  The reference maximum m a row's exponentials are taken
+// against only moves when a tile's maximum exceeds it by more than TAU = 8
+// (log2 units); otherwise the tile's exponentials are taken against the old
+// m and may reach 2^8.  The result is unchanged: l and the accumulator share
+// the same reference, and the final division cancels it.  This skips the
+// O(d) rescale of the accumulator on most tiles.
+//
+// Tiles in LDS: K and V are both row-major and swizzled (fa_tile.h).  K is
+// read as the A operand of S^T = K Q^T one 16-byte chunk per lane; V^T, the A
+// operand of O^T += V^T P^T, comes straight from the row-major V tile through
+// the hardware transpose read.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include "fa_internal.h"
+#include "fa_tile.h"
 
 namespace fa {
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
 constexpr int MAX_MASK_BLOCKS = 512;   // sparse: N <= 65536 with 128-blocks
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+constexpr float TAU = 8.f;             // lazy-rescale threshold (log2 units)
 
 // ---------------------------------------------------------------------------
 // bf16 forward.  D = head dim, BC = keys per tile, BR = 128 queries per
@@ -61,14 +59,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
     constexpr int KSTEPS = D / 16;         // k-steps of S^T over d
     constexpr int NKC = BC / 32;           // 32-key chunks per tile
     constexpr int NDB = D / 32;            // 32-wide d blocks of O^T
-    constexpr int KS = D + 8;              // LDS row stride of K (bf16)
-    constexpr int VS = BC + 4;             // LDS row stride of V^T (bf16)
-    constexpr int CPR = D / 8;             // 16-byte chunks per row
-    constexpr int CH = BC * CPR / 256;     // chunks per thread per tile
-    static_assert(CH * 256 == BC * CPR, "tile must split evenly over 256 threads");
 
-    __shared__ __attribute__((aligned(16))) bf16 ks[2][BC * KS];
-    __shared__ __attribute__((aligned(16))) bf16 vt[2][D * VS];
+    __shared__ __attribute__((aligned(16))) bf16 ks[2][BC * D];
+    __shared__ __attribute__((aligned(16))) bf16 vs[2][BC * D];
     __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
     __shared__ int bcount;
 
@@ -144,36 +137,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
             qreg[s] = bf16x8{};
     }
 
-    // ---- cooperative tile staging through registers
-    bf16x8 kreg[CH], vreg[CH];
+    TileStage<BC, D> kst, vst;
     auto load_tile = [&](int j) {
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-            const int cidx = tid + 256 * r;
-            const int row = cidx / CPR, col = (cidx % CPR) * 8;
-            const int key = j * BC + row;
-            if (key < N) {
-                kreg[r] = *(const bf16x8 *)(K + (size_t)key * D + col);
-                vreg[r] = *(const bf16x8 *)(V + (size_t)key * D + col);
-            } else {
-                kreg[r] = bf16x8{};
-                vreg[r] = bf16x8{};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-            const int cidx = tid + 256 * r;
-            const int row = cidx / CPR, col = (cidx % CPR) * 8;
-            *(bf16x8 *)&ks[buf][row * KS + col] = kreg[r];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vt[buf][(col + e) * VS + row] = vreg[r][e];
-        }
+        const int key0 = j * BC;
+        kst.load(K + (size_t)key0 * D, N - key0);
+        vst.load(V + (size_t)key0 * D, N - key0);
     };
 
-    float m = -INFINITY;   // running max (log2 units), same in both lane halves
+    float m = -INFINITY;   // reference max (log2 units), same in both lane halves
     float lsum = 0.f;      // running sum, partial over this lane half's keys
     f32x16 oacc[NDB];
 #pragma unroll
@@ -182,7 +153,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
 
     if (n_tiles > 0) {
         load_tile(tile_of(0));
-        store_tile(0);
+        kst.store(ks[0]);
+        vst.store(vs[0]);
     }
     __syncthreads();
 
@@ -201,10 +173,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
                 s[kc] = f32x16{};
-                const bf16 *krow = &ks[buf][(kc * 32 + l32) * KS + hf * 8];
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st)
-                    s[kc] = mfma_bf16(*(const bf16x8 *)(krow + st * 16), qreg[st], s[kc]);
+                    s[kc] = mfma_bf16(ld_row8<D>(ks[buf], kc * 32 + l32, st * 16 + hf * 8), qreg[st], s[kc]);
             }
             // masks: only tiles that cross the diagonal or the key length
             const bool need_mask = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
@@ -218,18 +189,24 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
                             s[kc][i] = -INFINITY;
                     }
             }
-            // running max
+            // tile max; move the reference only when it grows past TAU
             float mx = -INFINITY;
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     mx = fmaxf(mx, s[kc][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m, mx * c_log2);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m - m_use);
-            m = m_new;
+            const float mt = pair_max(mx) * c_log2;
+            if (__any(mt > m + TAU)) {
+                const float m_new = fmaxf(m, mt);
+                const float alpha = exp2_hw(m - m_new);   // 0 when m = -inf
+                m = m_new;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] *= alpha;
+            }
+            const float m_use = (m == -INFINITY) ? 0.f : m;
             // probabilities, row sum, bf16 operands for P V
             float rs = 0.f;
             bf16x8 pb[NKC][2];
@@ -237,37 +214,29 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float pv = fast_exp2(fmaf(s[kc][i], c_log2, -m_use));
+                    const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m_use));
                     rs += pv;
                     pb[kc][i / 8][i % 8] = (bf16)pv;
                 }
-            lsum = alpha * lsum + rs;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                oacc[db] *= alpha;
+            lsum += rs;
             // O^T += V_j^T P^T
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16 *vrow = &vt[buf][(db * 32 + l32) * VS + 4 * hf];
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const bf16 *src = vrow + kc * 32 + hh * 16;
-                        const bf16x4 a0 = *(const bf16x4 *)src;
-                        const bf16x4 a1 = *(const bf16x4 *)(src + 8);
-                        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        oacc[db] = mfma_bf16(a, pb[kc][hh], oacc[db]);
-                    }
-            }
+                    for (int hh = 0; hh < 2; ++hh)
+                        oacc[db] = mfma_bf16(ld_tr8<D>(vs[buf], kc * 32 + hh * 16, db * 32), pb[kc][hh], oacc[db]);
         }
-        if (t + 1 < n_tiles)
-            store_tile(buf ^ 1);
+        if (t + 1 < n_tiles) {
+            kst.store(ks[buf ^ 1]);
+            vst.store(vs[buf ^ 1]);
+        }
         __syncthreads();
     }
 
     // ---- epilogue: O = acc / l, LSE = ln2 (m + log2 l)
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float ltot = pair_sum(lsum);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (qrow < N) {
         bf16 *O = (bf16 *)p.o + head_off + (size_t)qrow * D;
@@ -282,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
                 *(bf16x4 *)(O + db * 32 + 8 * g + 4 * hf) = ov;
             }
         if (hf == 0)
-            p.lse[(size_t)bh * N + qrow] = ltot > 0.f ? LN2 * (m + __log2f(ltot)) : -INFINITY;
+            p.lse[(size_t)bh * N + qrow] = ltot > 0.f ? kLn2 * (m + __log2f(ltot)) : -INFINITY;
     }
 }
 
@@ -370,12 +339,12 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p, float c_log2
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float m_new = fmaxf(m, mx * c_log2);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m - m_use);
+            const float alpha = exp2_hw(m - m_use);
             m = m_new;
             float rs = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                s[i] = fast_exp2(fmaf(s[i], c_log2, -m_use));
+                s[i] = exp2_hw(fmaf(s[i], c_log2, -m_use));
                 rs += s[i];
             }
             lsum = alpha * lsum + rs;
@@ -403,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p, float c_log2
             for (int i = 0; i < 16; ++i)
                 O[db * 32 + 8 * (i / 4) + 4 * hf + (i % 4)] = oacc[db][i] * inv;
         if (hf == 0)
-            p.lse[(size_t)bh * N + qrow] = ltot > 0.f ? LN2 * (m + __log2f(ltot)) : -INFINITY;
+            p.lse[(size_t)bh * N + qrow] = ltot > 0.f ? kLn2 * (m + __log2f(ltot)) : -INFINITY;
     }
 }
 
@@ -414,7 +383,7 @@ static hipError_t launch_bf16_inst(const FwdArgs &a, hipStream_t s)
     const int n_qblk = (a.N + 127) / 128;
     const dim3 grid(a.B * a.H * n_qblk), block(256);
     FwdArgs args = a;
-    float c = a.scale * LOG2E;
+    float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     return hipLaunchKernel((const void *)&fwd_bf16_kernel<D, BC, CAUSAL, SPARSE>, grid, block,
                            kargs, 0, s);
@@ -450,7 +419,7 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal, hipStream_t s)
     const int n_qblk = (a.N + 127) / 128;
     const dim3 grid(a.B * a.H * n_qblk), block(256);
     FwdArgs args = a;
-    float c = a.scale * LOG2E;
+    float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     const void *fn;
     if (d == 64)
