@@ -189,6 +189,9 @@ def main(argv=None):
                     help="forward key tiles to time on the side ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="first run one plain device copy of MB MiB (a known-size kernel "
+                         "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -221,6 +224,15 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
 
     stages = ["fwd"] + (["bwd_dot", "bwd_dkdv", "bwd_dq"] if w.backward else [])
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def launch(stage, tile=args.tile):
         if stage == "fwd":

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
     const int bh = w / n_kb;
     const int kb = w % n_kb;               // causal: low key blocks have the most work
     const int b = bh / p.H;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hf = lane >> 5;
     const int k0 = kb * BKV;
     const int wk0 = k0 + wave * 32;
@@ -133,10 +133,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
 
     TileStage<BQ, D> qst, gst;
     float lse_r = INFINITY, dd_r = 0.f;    // threads < BQ stage one row's LSE and D
+    const __amdgpu_buffer_rsrc_t qrs = head_rsrc(Q, N, D), grs = head_rsrc(dO, N, D);
     auto load_tile = [&](int it) {
         const int qbase = it * BQ;
-        qst.load(Q + (size_t)qbase * D, N - qbase);
-        gst.load(dO + (size_t)qbase * D, N - qbase);
+        qst.load(qrs, qbase);
+        gst.load(grs, qbase);
         if (tid < BQ) {
             const int qi = qbase + tid;
             lse_r = INFINITY;              // rows past N: P = 0
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
     if (CAUSAL)
         qb = n_qblk - 1 - qb;
     const int b = bh / p.H;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hf = lane >> 5;
     const int q0 = qb * BR;
     const int wq0 = q0 + wave * 32;
@@ -305,10 +306,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
     const int n_tiles = (kv_end + BC - 1) / BC;
 
     TileStage<BC, D> kst, vst;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(K, N, D), vrs = head_rsrc(V, N, D);
     auto load_tile = [&](int t) {
-        const int key0 = t * BC;
-        kst.load(K + (size_t)key0 * D, N - key0);
-        vst.load(V + (size_t)key0 * D, N - key0);
+        kst.load(krs, t * BC);
+        vst.load(vrs, t * BC);
     };
     if (n_tiles > 0) {
         load_tile(0);

@@ -34,10 +34,11 @@
 // the same reference, and the final division cancels it.  This skips the
 // O(d) rescale of the accumulator on most tiles.
 //
-// Tiles in LDS: K and V are both row-major and swizzled (fa_tile.h).  K is
-// read as the A operand of S^T = K Q^T one 16-byte chunk per lane; V^T, the A
-// operand of O^T += V^T P^T, comes straight from the row-major V tile through
-// the hardware transpose read.
+// Tiles in LDS: K and V are both row-major and swizzled (fa_tile.h), copied
+// from HBM by direct buffer->LDS loads.  K is read as the A operand of
+// S^T = K Q^T one 16-byte chunk per lane; V^T, the A operand of
+// O^T += V^T P^T, comes straight from the row-major V tile through the
+// hardware transpose read.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -52,6 +53,9 @@ constexpr float TAU = 8.f;             // lazy-rescale threshold (log2 units)
 // ---------------------------------------------------------------------------
 // bf16 forward.  D = head dim, BC = keys per tile, BR = 128 queries per
 // workgroup.  SPARSE walks the nonzero 128-blocks of the workgroup's mask row.
+//
+// Tiles reach LDS by direct buffer->LDS loads into two stages; the loop is
+// unrolled by two so each half reads one stage while the other stage fills.
 template <int D, int BC, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log2)
 {
@@ -60,8 +64,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
     constexpr int NKC = BC / 32;           // 32-key chunks per tile
     constexpr int NDB = D / 32;            // 32-wide d blocks of O^T
 
-    __shared__ __attribute__((aligned(16))) bf16 ks[2][BC * D];
-    __shared__ __attribute__((aligned(16))) bf16 vs[2][BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 k0s[BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 v0s[BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 k1s[BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 v1s[BC * D];
     __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
     __shared__ int bcount;
 
@@ -76,7 +82,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
     const int b = bh / p.H;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hf = lane >> 5;
     const int q0 = qb * BR;
     const int wq0 = q0 + wave * 32;          // first query of this wave
@@ -84,8 +90,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
 
     const size_t head_off = (size_t)bh * N * D;
     const bf16 *Q = (const bf16 *)p.q + head_off;
-    const bf16 *K = (const bf16 *)p.k + head_off;
-    const bf16 *V = (const bf16 *)p.v + head_off;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc((const bf16 *)p.k + head_off, N, D);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc((const bf16 *)p.v + head_off, N, D);
 
     int kv_len = N;
     if (p.kv_lens) {
@@ -113,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
                 bcount = cnt;
         }
         __syncthreads();
-        n_tiles = bcount * TPB;
+        n_tiles = __builtin_amdgcn_readfirstlane(bcount) * TPB;
     } else {
         int kv_end = kv_len;
         if (CAUSAL)
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
     }
     auto tile_of = [&](int t) -> int {
         if constexpr (SPARSE)
-            return blist[t / TPB] * TPB + t % TPB;
+            return __builtin_amdgcn_readfirstlane(blist[t / TPB]) * TPB + t % TPB;
         else
             return t;
     };
@@ -137,11 +143,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
             qreg[s] = bf16x8{};
     }
 
-    TileStage<BC, D> kst, vst;
-    auto load_tile = [&](int j) {
-        const int key0 = j * BC;
-        kst.load(K + (size_t)key0 * D, N - key0);
-        vst.load(V + (size_t)key0 * D, N - key0);
+    TileDma<BC, D, 4> dma;
+    dma.init(wave);
+    auto issue = [&](int j, bf16 *kd, bf16 *vd) {
+        dma.issue(krs, j * BC, kd, wave);
+        dma.issue(vrs, j * BC, vd, wave);
     };
 
     float m = -INFINITY;   // reference max (log2 units), same in both lane halves
@@ -151,87 +157,87 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
     for (int db = 0; db < NDB; ++db)
         oacc[db] = f32x16{};
 
-    if (n_tiles > 0) {
-        load_tile(tile_of(0));
-        kst.store(ks[0]);
-        vst.store(vs[0]);
-    }
-    __syncthreads();
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
-        const int j = tile_of(t);
-        if (t + 1 < n_tiles)
-            load_tile(tile_of(t + 1));
-
+    auto compute = [&](int j, const bf16 *kt, const bf16 *vt) {
         const int kbase = j * BC;
         // whole tile above this wave's diagonal: nothing to add
-        const bool skip = CAUSAL && kbase > wq0 + 31;
-        if (!skip) {
-            // S^T = K_j Q^T
-            f32x16 s[NKC];
+        if (CAUSAL && kbase > wq0 + 31)
+            return;
+        // S^T = K_j Q^T
+        f32x16 s[NKC];
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                s[kc] = f32x16{};
+        for (int kc = 0; kc < NKC; ++kc) {
+            s[kc] = f32x16{};
 #pragma unroll
-                for (int st = 0; st < KSTEPS; ++st)
-                    s[kc] = mfma_bf16(ld_row8<D>(ks[buf], kc * 32 + l32, st * 16 + hf * 8), qreg[st], s[kc]);
-            }
-            // masks: only tiles that cross the diagonal or the key length
-            const bool need_mask = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
-            if (need_mask) {
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kbase + kc * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
-                        if (key >= kv_len || (CAUSAL && key > qrow))
-                            s[kc][i] = -INFINITY;
-                    }
-            }
-            // tile max; move the reference only when it grows past TAU
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, s[kc][i]);
-            const float mt = pair_max(mx) * c_log2;
-            if (__any(mt > m + TAU)) {
-                const float m_new = fmaxf(m, mt);
-                const float alpha = exp2_hw(m - m_new);   // 0 when m = -inf
-                m = m_new;
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    oacc[db] *= alpha;
-            }
-            const float m_use = (m == -INFINITY) ? 0.f : m;
-            // probabilities, row sum, bf16 operands for P V
-            float rs = 0.f;
-            bf16x8 pb[NKC][2];
+            for (int st = 0; st < KSTEPS; ++st)
+                s[kc] = mfma_bf16(ld_row8<D>(kt, kc * 32 + l32, st * 16 + hf * 8), qreg[st], s[kc]);
+        }
+        // masks: only tiles that cross the diagonal or the key length
+        if ((kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0)) {
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m_use));
-                    rs += pv;
-                    pb[kc][i / 8][i % 8] = (bf16)pv;
+                    const int key = kbase + kc * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
+                    if (key >= kv_len || (CAUSAL && key > qrow))
+                        s[kc][i] = -INFINITY;
                 }
-            lsum += rs;
-            // O^T += V_j^T P^T
+        }
+        // tile max; move the reference only when it grows past TAU
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                mx = fmaxf(mx, s[kc][i]);
+        const float mt = pair_max(mx) * c_log2;
+        if (__any(mt > m + TAU)) {
+            const float m_new = fmaxf(m, mt);
+            const float alpha = exp2_hw(m - m_new);   // 0 when m = -inf
+            m = m_new;
+            lsum *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
-                        oacc[db] = mfma_bf16(ld_tr8<D>(vs[buf], kc * 32 + hh * 16, db * 32), pb[kc][hh], oacc[db]);
+                oacc[db] *= alpha;
         }
-        if (t + 1 < n_tiles) {
-            kst.store(ks[buf ^ 1]);
-            vst.store(vs[buf ^ 1]);
-        }
+        const float m_use = (m == -INFINITY) ? 0.f : m;
+        // probabilities (fp32 row sum), bf16 operands for P V
+        float rs = 0.f;
+        bf16x8 pb[NKC][2];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m_use));
+                rs += pv;
+                pb[kc][i / 8][i % 8] = (bf16)pv;
+            }
+        lsum += rs;
+        // O^T += V_j^T P^T
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    oacc[db] = mfma_bf16(ld_tr8<D>(vt, kc * 32 + hh * 16, db * 32), pb[kc][hh], oacc[db]);
+    };
+
+    if (n_tiles > 0)
+        issue(tile_of(0), k0s, v0s);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < n_tiles; t += 2) {
+        if (t + 1 < n_tiles)
+            issue(tile_of(t + 1), k1s, v1s);
+        compute(tile_of(t), k0s, v0s);
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 >= n_tiles)
+            break;
+        if (t + 2 < n_tiles)
+            issue(tile_of(t + 2), k0s, v0s);
+        compute(tile_of(t + 1), k1s, v1s);
+        wait_vmem();
         __syncthreads();
     }
 

@@ -25,6 +25,7 @@ namespace fa {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -91,10 +92,21 @@ __device__ __forceinline__ bf16x8 ld_tr8(const bf16 *t, int row0, int col0)
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Cooperative copy of a ROWS x D bf16 tile from global memory (rows of D
-// contiguous elements) into a swizzled LDS tile, staged through registers so
-// that the global loads of the next tile can be in flight during compute.
-// Rows at or past `valid` are filled with zeros.
+// Buffer resource over one head's [N][D] bf16 rows: loads past the last row
+// return zeros (the hardware range check), so ragged tiles need no
+// predication.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16 *base, int rows, int D)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rows * D * 2, 0x00020000);
+}
+
+// wave index as a scalar, so that branches on it are uniform
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Cooperative copy of a ROWS x D bf16 tile (rows row0 .. row0+ROWS-1 of a
+// head) into a swizzled LDS tile, staged through registers so that the
+// global loads of the next tile are in flight during compute.  Rows past the
+// head's end read as zeros.
 template <int ROWS, int D>
 struct TileStage {
     static constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -102,13 +114,16 @@ struct TileStage {
     static_assert(CH * 256 == ROWS * CPR, "tile must split evenly over 256 threads");
     bf16x8 r[CH];
 
-    __device__ __forceinline__ void load(const bf16 *g, int valid)
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int row0)
     {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int cidx = threadIdx.x + 256 * i;
             const int row = cidx / CPR, col = (cidx % CPR) * 8;
-            r[i] = row < valid ? *(const bf16x8 *)(g + (size_t)row * D + col) : bf16x8{};
+            const unsigned off = (unsigned)(((row0 + row) * D + col) * 2);
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            r[i] = __builtin_bit_cast(bf16x8, v);
         }
     }
     __device__ __forceinline__ void store(bf16 *t) const
@@ -121,5 +136,52 @@ struct TileStage {
         }
     }
 };
+
+// one 16-byte-per-lane buffer->LDS load (wrapped in a plain device function:
+// used directly inside kernel templates, the builtin kept the host pass from
+// emitting those kernels' handles)
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, bf16 *lds, unsigned voff,
+                                                int soff)
+{
+    typedef void __attribute__((address_space(3))) lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+
+// Direct global -> LDS tile copy (buffer_load_dwordx4 ... lds, no register
+// staging).  One such load writes the 16 bytes of lane L at LDS address
+// M0 + 16 L, so each wave instruction fills 1 KB of the tile in physical
+// order; the swizzle is applied on the global side: the lane that owns
+// physical chunk pc of row r loads logical chunk pc ^ swz(r).  The WAVES
+// waves of the workgroup split the tile's 1 KB segments round-robin.  The
+// copy is asynchronous: wait on vmcnt, then barrier, before reading.
+template <int ROWS, int D, int WAVES>
+struct TileDma {
+    static constexpr int CPR = D / 8;                      // 16-byte chunks per row
+    static constexpr int SEGS = ROWS * CPR / 64;           // 1 KB segments per tile
+    static constexpr int PER_WAVE = SEGS / WAVES;
+    static_assert(PER_WAVE * WAVES == SEGS, "tile must split evenly over the waves");
+    unsigned voff[PER_WAVE];                               // per-lane byte offsets within the tile
+
+    __device__ __forceinline__ void init(int wave)
+    {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int chunk = (wave + WAVES * i) * 64 + lane;      // physical chunk in tile
+            const int row = chunk / CPR, pc = chunk % CPR;
+            voff[i] = (unsigned)((row * D + ((pc ^ swz<D>(row)) << 3)) * 2);
+        }
+    }
+    // copy rows row0 .. row0+ROWS-1 of the head behind rs into tile t
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int row0, bf16 *t, int wave) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i)
+            buffer_to_lds16(rs, t + (wave + WAVES * i) * 512, voff[i], row0 * D * 2);
+    }
+};
+
+// wait until every vector-memory load of this wave (including LDS DMA) landed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 } // namespace fa

@@ -143,3 +143,18 @@ def test_python_binding_checks_shapes():
         fa.fwd(q.view(8, 64), q.view(8, 64), q.view(8, 64))
     with pytest.raises(ValueError):
         fa.fwd(q.half(), q.half(), q.half())
+
+
+def test_library_has_no_unresolved_kernels():
+    """Every kernel the launchers reference must be defined in libfa.so (a
+    missing host-side kernel handle only shows as an undefined symbol)."""
+    import shutil
+    import subprocess
+
+    fa = pytest.importorskip("exact_io_aware_36_amd")
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-u", fa.library_path], capture_output=True, text=True).stdout
+    bad = [ln for ln in out.splitlines() if "_ZN2fa" in ln]
+    assert not bad, bad
