@@ -81,9 +81,9 @@ def floor_bytes(stage, B, H, N, d, elem=2) -> float:
     rows = B * H * N * 4
     return {
         "fwd": 4 * t + rows,                 # Q, K, V in; O out; LSE out
-        "bwd_dot": 2 * t + rows,             # O, dO in; D out
-        "bwd_dkdv": 6 * t + 2 * rows,        # Q, K, V, dO, LSE, D in; dK, dV out
-        "bwd_dq": 5 * t + 2 * rows,          # Q, K, V, dO, LSE, D in; dQ out
+        "bwd_dot": 2 * t + 3 * rows,         # O, dO, LSE in; D, LSE*log2e out
+        "bwd_dkdv": 6 * t + 2 * rows,        # Q, K, V, dO, LSE*log2e, D in; dK, dV out
+        "bwd_dq": 5 * t + 2 * rows,          # Q, K, V, dO, LSE*log2e, D in; dQ out
     }[stage]
 
 
@@ -242,7 +242,7 @@ def main(argv=None):
                 fa.fa_fwd_ex(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=lens,
                              tile_n=tile)
         elif stage == "bwd_dot":
-            fa.fa_bwd_preprocess(o, dout, ws)
+            fa.fa_bwd_preprocess(o, dout, lse, ws)
         elif stage == "bwd_dkdv":
             fa.fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, ws, causal=w.causal, scale=w.scale,
                            kv_lens=lens)

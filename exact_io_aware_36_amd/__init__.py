@@ -3,9 +3,9 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/fa.h.  The functions named like
 the C entry points (fa_fwd, fa_fwd_ex, fa_bwd, fa_bwd_workspace_bytes,
-fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_fwd_blocksparse, fa_status_str) take torch device tensors, read their
-shapes and pointers and call the C function of the same name on the current
-torch stream (or the stream given).  fwd, bwd and fwd_blocksparse are the same
+fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_fwd_blocksparse, fa_status_str)
+take torch device tensors, read their shapes and pointers and call the C
+function of the same name on the current torch stream (or the stream given).  fwd, bwd and fwd_blocksparse are the same
 calls with the outputs (and the backward workspace) allocated by torch.
 
 There is no fallback: importing this package raises if libfa.so has not been
@@ -67,7 +67,7 @@ _lib.fa_bwd.restype = _i
 _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                         _vp, _i, _vp, _sz, _vp]
 _lib.fa_bwd_preprocess.restype = _i
-_lib.fa_bwd_preprocess.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+_lib.fa_bwd_preprocess.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]
 _lib.fa_bwd_dkdv.restype = _i
 _lib.fa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i,
                              _vp, _sz, _vp]
@@ -183,11 +183,11 @@ def _ws_bytes(workspace):
     return workspace.numel() * workspace.element_size() if workspace is not None else 0
 
 
-def fa_bwd_preprocess(o, dout, workspace, stream=None):
+def fa_bwd_preprocess(o, dout, lse, workspace, stream=None):
     B, H, N, d = _shape(o)
     _same(o, dout)
-    rc = _lib.fa_bwd_preprocess(_ptr(o), _ptr(dout), B, H, N, d, _dtype(o), _ptr(workspace),
-                                _ws_bytes(workspace), _stream(o, stream))
+    rc = _lib.fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(lse), B, H, N, d, _dtype(o),
+                                _ptr(workspace), _ws_bytes(workspace), _stream(o, stream))
     _check_rc(rc, "fa_bwd_preprocess")
 
 

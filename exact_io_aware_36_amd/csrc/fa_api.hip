@@ -80,12 +80,14 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
     return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, causal, scale, kv_lens, dtype, 0, stream);
 }
 
+// workspace: D then LSE * log2(e), each fp32 [B][H][N] rounded up to 256 B
+static size_t ws_region(int B, int H, int N) { return ((size_t)B * H * N * sizeof(float) + 255) / 256 * 256; }
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d)
 {
     if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128))
         return 0;
-    const size_t bytes = (size_t)B * H * N * sizeof(float);
-    return (bytes + 255) / 256 * 256;
+    return 2 * ws_region(B, H, N);
 }
 
 // Shared checks of fa_bwd and its stages.  A stage that does not use one of
@@ -121,21 +123,25 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
                              workspace, workspace_bytes);
     if (st != FA_OK)
         return st;
-    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, H, N, scale, kv_lens};
+    float *ws = (float *)workspace;
+    float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, ws, ws2, B, H, N, scale, kv_lens};
     return from_hip(fa::launch_bwd_bf16(a, d, causal != 0, (hipStream_t)stream));
 }
 
-fa_status fa_bwd_preprocess(const void *o, const void *dout, int B, int H, int N, int d,
-                            fa_dtype dtype, void *workspace, size_t workspace_bytes,
+fa_status fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, int H,
+                            int N, int d, fa_dtype dtype, void *workspace, size_t workspace_bytes,
                             fa_stream_t stream)
 {
     // o and dout stand in for every other tensor pointer of the full check
-    fa_status st = check_bwd(o, o, o, o, dout, (const float *)workspace, o, o, o, B, H, N, d, 1.f,
-                             nullptr, dtype, workspace, workspace_bytes);
+    fa_status st = check_bwd(o, o, o, o, dout, lse, o, o, o, B, H, N, d, 1.f, nullptr, dtype,
+                             workspace, workspace_bytes);
     if (st != FA_OK)
         return st;
-    fa::BwdArgs a{nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr,
-                  (float *)workspace, B, H, N, 1.f, nullptr};
+    float *ws = (float *)workspace;
+    float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
+    fa::BwdArgs a{nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr, ws, ws2,
+                  B, H, N, 1.f, nullptr};
     return from_hip(fa::launch_bwd_stage(a, d, false, fa::BwdStage::Dot, (hipStream_t)stream));
 }
 
@@ -148,8 +154,9 @@ fa_status fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *d
                              dtype, workspace, workspace_bytes);
     if (st != FA_OK)
         return st;
-    fa::BwdArgs a{q, k, v, nullptr, dout, lse, nullptr, dk, dv, (float *)workspace, B, H, N, scale,
-                  kv_lens};
+    float *ws = (float *)workspace;
+    float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
+    fa::BwdArgs a{q, k, v, nullptr, dout, lse, nullptr, dk, dv, ws, ws2, B, H, N, scale, kv_lens};
     return from_hip(fa::launch_bwd_stage(a, d, causal != 0, fa::BwdStage::DkDv, (hipStream_t)stream));
 }
 
@@ -162,8 +169,10 @@ fa_status fa_bwd_dq(const void *q, const void *k, const void *v, const void *dou
                              dtype, workspace, workspace_bytes);
     if (st != FA_OK)
         return st;
-    fa::BwdArgs a{q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, (float *)workspace, B, H, N,
-                  scale, kv_lens};
+    float *ws = (float *)workspace;
+    float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
+    fa::BwdArgs a{q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, ws, ws2, B, H, N, scale,
+                  kv_lens};
     return from_hip(fa::launch_bwd_stage(a, d, causal != 0, fa::BwdStage::Dq, (hipStream_t)stream));
 }
 

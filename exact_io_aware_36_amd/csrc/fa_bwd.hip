@@ -13,7 +13,8 @@
 // dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
 // Three launches on one stream:
-//   1. bwd_dot_kernel: D_i = dO_i . O_i (fp32) into the workspace.
+//   1. bwd_dot_kernel: D_i = dO_i . O_i (fp32) and LSE_i * log2(e) into the
+//      workspace.
 //   2. bwd_dkdv_kernel: keys outer.  A workgroup owns 128 keys of one
 //      (b, h) (32 per wave, held in registers as MFMA operands) and walks the
 //      query tiles, accumulating dK and dV in registers.
@@ -40,11 +41,13 @@ namespace fa {
 
 namespace {
 
-// D_i = dO_i . O_i in fp32 -----------------------------------------------
+// D_i = dO_i . O_i in fp32, and the row's LSE in log2 units ----------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16 *__restrict__ o,
                                                       const bf16 *__restrict__ dout,
-                                                      float *__restrict__ dvec, int rows)
+                                                      const float *__restrict__ lse,
+                                                      float *__restrict__ dvec,
+                                                      float *__restrict__ lse2, int rows)
 {
     constexpr int CPR = D / 8;             // threads per row
     constexpr int RPB = 256 / CPR;         // rows per block
@@ -61,23 +64,34 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16 *__restrict__ o
 #pragma unroll
     for (int off = CPR / 2; off > 0; off >>= 1)
         acc += __shfl_xor(acc, off);
-    if (r < rows && threadIdx.x % CPR == 0)
+    if (r < rows && threadIdx.x % CPR == 0) {
         dvec[r] = acc;
+        const float l = lse[r];
+        lse2[r] = (l == -INFINITY) ? INFINITY : l * kLog2e;   // a row with no key: P = 0
+    }
 }
 
 // dK, dV: keys outer ------------------------------------------------------
+// Q and dO tiles (and their rows' LSE and D) reach LDS by direct buffer->LDS
+// loads into two stages; the loop is unrolled by two.  Query rows past N read
+// as zeros (Q, dO, LSE, D all 0), which makes their dS and P^T dO terms 0.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log2)
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs p, float c_log2)
 {
     constexpr int BKV = 128, BQ = 64;
     constexpr int KSTEPS = D / 16;
     constexpr int NQC = BQ / 32;           // 32-query chunks per tile
     constexpr int NDB = D / 32;
+    constexpr int G = D == 64 ? 1 : NQC;   // chunks processed together
 
-    __shared__ __attribute__((aligned(16))) bf16 qs[2][BQ * D];
-    __shared__ __attribute__((aligned(16))) bf16 dos[2][BQ * D];
-    __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
-    __shared__ __attribute__((aligned(16))) float dd_s[2][BQ];
+    __shared__ __attribute__((aligned(1024))) bf16 q0s[BQ * D];
+    __shared__ __attribute__((aligned(1024))) bf16 g0s[BQ * D];
+    __shared__ __attribute__((aligned(1024))) bf16 q1s[BQ * D];
+    __shared__ __attribute__((aligned(1024))) bf16 g1s[BQ * D];
+    __shared__ __attribute__((aligned(256))) float l0s[BQ];
+    __shared__ __attribute__((aligned(256))) float d0s[BQ];
+    __shared__ __attribute__((aligned(256))) float l1s[BQ];
+    __shared__ __attribute__((aligned(256))) float d1s[BQ];
 
     const int N = p.N;
     const int n_kb = (N + BKV - 1) / BKV;
@@ -93,12 +107,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
     const int key = wk0 + l32;
 
     const size_t head_off = (size_t)bh * N * D;
-    const bf16 *Q = (const bf16 *)p.q + head_off;
     const bf16 *K = (const bf16 *)p.k + head_off;
     const bf16 *V = (const bf16 *)p.v + head_off;
-    const bf16 *dO = (const bf16 *)p.dout + head_off;
-    const float *LSE = p.lse + (size_t)bh * N;
-    const float *Dv = p.dvec + (size_t)bh * N;
+    const __amdgpu_buffer_rsrc_t qrs = head_rsrc((const bf16 *)p.q + head_off, N, D);
+    const __amdgpu_buffer_rsrc_t grs = head_rsrc((const bf16 *)p.dout + head_off, N, D);
+    const __amdgpu_buffer_rsrc_t lrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(p.lse2 + (size_t)bh * N), (short)0, N * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t drs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(p.dvec + (size_t)bh * N), (short)0, N * 4, 0x00020000);
 
     int kv_len = N;
     if (p.kv_lens) {
@@ -131,90 +147,88 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
     const int qt_end = (k0 < kv_len) ? n_qt : qt_begin;   // no allowed key: nothing to do
     const bool wave_live = wk0 < kv_len;
 
-    TileStage<BQ, D> qst, gst;
-    float lse_r = INFINITY, dd_r = 0.f;    // threads < BQ stage one row's LSE and D
-    const __amdgpu_buffer_rsrc_t qrs = head_rsrc(Q, N, D), grs = head_rsrc(dO, N, D);
-    auto load_tile = [&](int it) {
+    TileDma<BQ, D, 4> dma;
+    dma.init(wave);
+    auto issue = [&](int it, bf16 *qd, bf16 *gd, float *ld, float *dd) {
         const int qbase = it * BQ;
-        qst.load(qrs, qbase);
-        gst.load(grs, qbase);
-        if (tid < BQ) {
-            const int qi = qbase + tid;
-            lse_r = INFINITY;              // rows past N: P = 0
-            dd_r = 0.f;
-            if (qi < N) {
-                const float l = LSE[qi];
-                lse_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
-                dd_r = Dv[qi];
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        qst.store(qs[buf]);
-        gst.store(dos[buf]);
-        if (tid < BQ) {
-            lse_s[buf][tid] = lse_r;
-            dd_s[buf][tid] = dd_r;
-        }
+        dma.issue(qrs, qbase, qd, wave);
+        dma.issue(grs, qbase, gd, wave);
+        if (wave == 0)
+            buffer_to_lds4(lrs, ld, lane * 4, qbase * 4);
+        else if (wave == 1)
+            buffer_to_lds4(drs, dd, lane * 4, qbase * 4);
     };
 
-    if (qt_begin < qt_end) {
-        load_tile(qt_begin);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int it = qt_begin; it < qt_end; ++it) {
-        const int buf = (it - qt_begin) & 1;
+    auto compute = [&](int it, const bf16 *qt, const bf16 *gt, const float *lt, const float *dt) {
         const int qbase = it * BQ;
-        if (it + 1 < qt_end)
-            load_tile(it + 1);
-
-        const bool skip = !wave_live || (CAUSAL && qbase + BQ - 1 < wk0);
-        if (!skip) {
-            f32x16 s[NQC], dp[NQC];
+        if (!wave_live || (CAUSAL && qbase + BQ - 1 < wk0))
+            return;
+        const bool need_mask = (CAUSAL && qbase < wk0 + 31) || (wk0 + 32 > kv_len);
+        // G 32-query chunks at a time (G = 1 at d = 64 keeps the kernel within
+        // 256 registers for two waves per SIMD; G = 2 at d = 128, where the
+        // kernel runs one wave per SIMD and more independent MFMA chains pay):
+        // S, dP, then P and dS, then dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
-            for (int qc = 0; qc < NQC; ++qc) {
-                s[qc] = f32x16{};
-                dp[qc] = f32x16{};
+        for (int q0c = 0; q0c < NQC; q0c += G) {
+            f32x16 s[G], dp[G];
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                const int qc = q0c + u;
+                s[u] = f32x16{};
+                dp[u] = f32x16{};
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st) {
-                    s[qc] = mfma_bf16(ld_row8<D>(qs[buf], qc * 32 + l32, st * 16 + hf * 8), kreg[st], s[qc]);
-                    dp[qc] = mfma_bf16(ld_row8<D>(dos[buf], qc * 32 + l32, st * 16 + hf * 8), vreg[st], dp[qc]);
+                    s[u] = mfma_bf16(ld_row8<D>(qt, qc * 32 + l32, st * 16 + hf * 8), kreg[st], s[u]);
+                    dp[u] = mfma_bf16(ld_row8<D>(gt, qc * 32 + l32, st * 16 + hf * 8), vreg[st], dp[u]);
                 }
             }
-            const bool need_mask = (CAUSAL && qbase < wk0 + 31) || (wk0 + 32 > kv_len);
-            bf16x8 pb[NQC][2], dsb[NQC][2];
+            bf16x8 pb[G][2], dsb[G][2];
 #pragma unroll
-            for (int qc = 0; qc < NQC; ++qc)
+            for (int u = 0; u < G; ++u)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int trow = qc * 32 + 8 * g + 4 * hf;
-                    const f32x4 l4 = *(const f32x4 *)&lse_s[buf][trow];
-                    const f32x4 d4 = *(const f32x4 *)&dd_s[buf][trow];
+                    const int trow = (q0c + u) * 32 + 8 * g + 4 * hf;
+                    const f32x4 l4 = *(const f32x4 *)&lt[trow];
+                    const f32x4 d4 = *(const f32x4 *)&dt[trow];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 4 * g + e;
-                        float pv = exp2_hw(fmaf(s[qc][i], c_log2, -l4[e]));
+                        float pv = exp2_hw(fmaf(s[u][i], c_log2, -l4[e]));
                         if (need_mask && (key >= kv_len || (CAUSAL && key > qbase + trow + e)))
                             pv = 0.f;
-                        const float ds = pv * (dp[qc][i] - d4[e]);
-                        pb[qc][i / 8][i % 8] = (bf16)pv;
-                        dsb[qc][i / 8][i % 8] = (bf16)ds;
+                        pb[u][i / 8][i % 8] = (bf16)pv;
+                        dsb[u][i / 8][i % 8] = (bf16)(pv * (dp[u][i] - d4[e]));
                     }
                 }
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int qc = 0; qc < NQC; ++qc)
+                for (int u = 0; u < G; ++u)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        dv_acc[db] = mfma_bf16(ld_tr8<D>(dos[buf], qc * 32 + hh * 16, db * 32), pb[qc][hh], dv_acc[db]);
-                        dk_acc[db] = mfma_bf16(ld_tr8<D>(qs[buf], qc * 32 + hh * 16, db * 32), dsb[qc][hh], dk_acc[db]);
+                        const int qc = q0c + u;
+                        dv_acc[db] = mfma_bf16(ld_tr8<D>(gt, qc * 32 + hh * 16, db * 32), pb[u][hh], dv_acc[db]);
+                        dk_acc[db] = mfma_bf16(ld_tr8<D>(qt, qc * 32 + hh * 16, db * 32), dsb[u][hh], dk_acc[db]);
                     }
         }
+    };
+
+    if (qt_begin < qt_end)
+        issue(qt_begin, q0s, g0s, l0s, d0s);
+    wait_vmem();
+    __syncthreads();
+    for (int it = qt_begin; it < qt_end; it += 2) {
         if (it + 1 < qt_end)
-            store_tile(buf ^ 1);
+            issue(it + 1, q1s, g1s, l1s, d1s);
+        compute(it, q0s, g0s, l0s, d0s);
+        wait_vmem();
+        __syncthreads();
+        if (it + 1 >= qt_end)
+            break;
+        if (it + 2 < qt_end)
+            issue(it + 2, q0s, g0s, l0s, d0s);
+        compute(it + 1, q1s, g1s, l1s, d1s);
+        wait_vmem();
         __syncthreads();
     }
 
@@ -239,16 +253,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs p, float c_log
 }
 
 // dQ: queries outer ---------------------------------------------------------
+// K and V tiles reach LDS by direct buffer->LDS loads into two stages.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
+__global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_kernel(BwdArgs p, float c_log2)
 {
     constexpr int BR = 128, BC = 64;
     constexpr int KSTEPS = D / 16;
     constexpr int NKC = BC / 32;
     constexpr int NDB = D / 32;
 
-    __shared__ __attribute__((aligned(16))) bf16 ks[2][BC * D];
-    __shared__ __attribute__((aligned(16))) bf16 vs[2][BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 k0s[BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 v0s[BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 k1s[BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 v1s[BC * D];
 
     const int N = p.N;
     const int n_qblk = (N + BR - 1) / BR;
@@ -267,9 +284,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
 
     const size_t head_off = (size_t)bh * N * D;
     const bf16 *Q = (const bf16 *)p.q + head_off;
-    const bf16 *K = (const bf16 *)p.k + head_off;
-    const bf16 *V = (const bf16 *)p.v + head_off;
     const bf16 *dO = (const bf16 *)p.dout + head_off;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc((const bf16 *)p.k + head_off, N, D);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc((const bf16 *)p.v + head_off, N, D);
 
     int kv_len = N;
     if (p.kv_lens) {
@@ -290,8 +307,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
     }
     float lse2 = INFINITY, dval = 0.f;
     if (qrow < N) {
-        const float l = p.lse[(size_t)bh * N + qrow];
-        lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        lse2 = p.lse2[(size_t)bh * N + qrow];
         dval = p.dvec[(size_t)bh * N + qrow];
     }
 
@@ -305,62 +321,60 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs p, float c_log2)
         kv_end = min(kv_end, q0 + BR);
     const int n_tiles = (kv_end + BC - 1) / BC;
 
-    TileStage<BC, D> kst, vst;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc(K, N, D), vrs = head_rsrc(V, N, D);
-    auto load_tile = [&](int t) {
-        kst.load(krs, t * BC);
-        vst.load(vrs, t * BC);
+    TileDma<BC, D, 4> dma;
+    dma.init(wave);
+    auto issue = [&](int t, bf16 *kd, bf16 *vd) {
+        dma.issue(krs, t * BC, kd, wave);
+        dma.issue(vrs, t * BC, vd, wave);
     };
-    if (n_tiles > 0) {
-        load_tile(0);
-        kst.store(ks[0]);
-        vst.store(vs[0]);
-    }
-    __syncthreads();
 
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
+    auto compute = [&](int t, const bf16 *kt, const bf16 *vt) {
         const int kbase = t * BC;
-        if (t + 1 < n_tiles)
-            load_tile(t + 1);
-
-        const bool skip = CAUSAL && kbase > wq0 + 31;
-        if (!skip) {
-            f32x16 s[NKC], dp[NKC];
+        if (CAUSAL && kbase > wq0 + 31)
+            return;
+        const bool need_mask = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
+        // one 32-key chunk at a time: S^T, dP^T, dS^T, then dQ^T += K^T dS^T
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                s[kc] = f32x16{};
-                dp[kc] = f32x16{};
+        for (int kc = 0; kc < NKC; ++kc) {
+            f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-                for (int st = 0; st < KSTEPS; ++st) {
-                    s[kc] = mfma_bf16(ld_row8<D>(ks[buf], kc * 32 + l32, st * 16 + hf * 8), qreg[st], s[kc]);
-                    dp[kc] = mfma_bf16(ld_row8<D>(vs[buf], kc * 32 + l32, st * 16 + hf * 8), greg[st], dp[kc]);
-                }
+            for (int st = 0; st < KSTEPS; ++st) {
+                s = mfma_bf16(ld_row8<D>(kt, kc * 32 + l32, st * 16 + hf * 8), qreg[st], s);
+                dp = mfma_bf16(ld_row8<D>(vt, kc * 32 + l32, st * 16 + hf * 8), greg[st], dp);
             }
-            const bool need_mask = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
-            bf16x8 dsb[NKC][2];
+            bf16x8 dsb[2];
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int kj = kbase + kc * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
-                    float pv = exp2_hw(fmaf(s[kc][i], c_log2, -lse2));
-                    if (need_mask && (kj >= kv_len || (CAUSAL && kj > qrow)))
-                        pv = 0.f;
-                    dsb[kc][i / 8][i % 8] = (bf16)(pv * (dp[kc][i] - dval));
-                }
+            for (int i = 0; i < 16; ++i) {
+                const int kj = kbase + kc * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
+                float pv = exp2_hw(fmaf(s[i], c_log2, -lse2));
+                if (need_mask && (kj >= kv_len || (CAUSAL && kj > qrow)))
+                    pv = 0.f;
+                dsb[i / 8][i % 8] = (bf16)(pv * (dp[i] - dval));
+            }
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
-                        dq_acc[db] = mfma_bf16(ld_tr8<D>(ks[buf], kc * 32 + hh * 16, db * 32), dsb[kc][hh], dq_acc[db]);
+                for (int hh = 0; hh < 2; ++hh)
+                    dq_acc[db] = mfma_bf16(ld_tr8<D>(kt, kc * 32 + hh * 16, db * 32), dsb[hh], dq_acc[db]);
         }
-        if (t + 1 < n_tiles) {
-            kst.store(ks[buf ^ 1]);
-            vst.store(vs[buf ^ 1]);
-        }
+    };
+
+    if (n_tiles > 0)
+        issue(0, k0s, v0s);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < n_tiles; t += 2) {
+        if (t + 1 < n_tiles)
+            issue(t + 1, k1s, v1s);
+        compute(t, k0s, v0s);
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 >= n_tiles)
+            break;
+        if (t + 2 < n_tiles)
+            issue(t + 2, k0s, v0s);
+        compute(t + 1, k1s, v1s);
+        wait_vmem();
         __syncthreads();
     }
 
@@ -385,8 +399,9 @@ hipError_t launch_dot(const BwdArgs &a, hipStream_t s)
     const int rows = a.B * a.H * a.N;
     constexpr int RPB = 256 / (D / 8);
     const bf16 *o = (const bf16 *)a.o, *g = (const bf16 *)a.dout;
-    float *dvec = a.dvec;
-    void *kargs[] = {&o, &g, &dvec, (void *)&rows};
+    const float *lse = a.lse;
+    float *dvec = a.dvec, *lse2 = a.lse2;
+    void *kargs[] = {&o, &g, &lse, &dvec, &lse2, (void *)&rows};
     return hipLaunchKernel((const void *)&bwd_dot_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256),
                            kargs, 0, s);
 }

@@ -24,6 +24,7 @@ struct BwdArgs {
     const float *lse;
     void *dq, *dk, *dv;
     float *dvec;            // workspace: D_i = dO_i . O_i, fp32 [B][H][N]
+    float *lse2;            // workspace: LSE_i * log2(e) (+inf where LSE = -inf)
     int B, H, N;
     float scale;
     const int32_t *kv_lens;

@@ -147,6 +147,14 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, bf16 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)lds, 16, voff, soff, 0, 0);
 }
 
+// one 4-byte-per-lane buffer->LDS load: 64 floats per wave instruction
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rs, float *lds, unsigned voff,
+                                               int soff)
+{
+    typedef void __attribute__((address_space(3))) lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)lds, 4, voff, soff, 0, 0);
+}
+
 // Direct global -> LDS tile copy (buffer_load_dwordx4 ... lds, no register
 // staging).  One such load writes the 16 bytes of lane L at LDS address
 // M0 + 16 L, so each wave instruction fills 1 KB of the tile in physical

@@ -104,9 +104,10 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
                     fa_stream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (the per-row
- * D_i = dO_i . O_i of the backward, fp32 [B][H][N], rounded up to 256 B).
- * Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd needs for these sizes: two fp32
+ * [B][H][N] row vectors, each rounded up to 256 B -- the backward's
+ * D_i = dO_i . O_i and the stored LSE_i rescaled to log2 units.  Returns 0
+ * for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -137,15 +138,17 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
  * and in this order (results equal fa_bwd's bit for bit).  Useful to time
  * or overlap the stages separately.  Arguments mean what they mean for
  * fa_bwd; the workspace must be the same buffer for all three calls.
- *   fa_bwd_preprocess: workspace <- D_i = dO_i . O_i (fp32 [B][H][N]).
- *   fa_bwd_dkdv:       dK, dV from Q, K, V, dO, LSE and the workspace
+ *   fa_bwd_preprocess: workspace <- D_i = dO_i . O_i and LSE_i * log2(e).
+ *   fa_bwd_dkdv:       dK, dV from Q, K, V, dO and the workspace
  *                      (keys-outer kernel).
- *   fa_bwd_dq:         dQ from Q, K, V, dO, LSE and the workspace
+ *   fa_bwd_dq:         dQ from Q, K, V, dO and the workspace
  *                      (queries-outer kernel).
+ * fa_bwd_dkdv and fa_bwd_dq read the LSE only through the workspace; their
+ * lse argument is still checked (non-NULL, aligned).
  * Errors: as fa_bwd.
  */
-fa_status fa_bwd_preprocess(const void *o, const void *dout, int B, int H, int N, int d,
-                            fa_dtype dtype, void *workspace, size_t workspace_bytes,
+fa_status fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, int H,
+                            int N, int d, fa_dtype dtype, void *workspace, size_t workspace_bytes,
                             fa_stream_t stream);
 fa_status fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
                       const float *lse, void *dk, void *dv, int B, int H, int N, int d,

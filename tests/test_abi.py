@@ -60,9 +60,10 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.fa_bwd_workspace_bytes(1, 16, 16384, 128) == 16 * 16384 * 4
-    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256          # rounded up
-    assert lib.fa_bwd_workspace_bytes(16, 16, 512, 64) == 16 * 16 * 512 * 4
+    # two fp32 [B, H, N] row vectors, each rounded up to 256 bytes
+    assert lib.fa_bwd_workspace_bytes(1, 16, 16384, 128) == 2 * 16 * 16384 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64) == 2 * 256
+    assert lib.fa_bwd_workspace_bytes(16, 16, 512, 64) == 2 * 16 * 16 * 512 * 4
     assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
     assert lib.fa_bwd_workspace_bytes(1, 1, 1, 96) == 0
 
