@@ -176,10 +176,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
                 const int qc = q0c + u;
                 s[u] = f32x16{};
                 dp[u] = f32x16{};
+                // operands first, then the products: keeps the scheduler from
+                // pairing each LDS read with its MFMA (which exposes LDS latency)
+                bf16x8 qa[KSTEPS], ga[KSTEPS];
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st) {
-                    s[u] = mfma_bf16(ld_row8<D>(qt, qc * 32 + l32, st * 16 + hf * 8), kreg[st], s[u]);
-                    dp[u] = mfma_bf16(ld_row8<D>(gt, qc * 32 + l32, st * 16 + hf * 8), vreg[st], dp[u]);
+                    qa[st] = ld_row8<D>(qt, qc * 32 + l32, st * 16 + hf * 8);
+                    ga[st] = ld_row8<D>(gt, qc * 32 + l32, st * 16 + hf * 8);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int st = 0; st < KSTEPS; ++st) {
+                    s[u] = mfma_bf16(qa[st], kreg[st], s[u]);
+                    dp[u] = mfma_bf16(ga[st], vreg[st], dp[u]);
                 }
             }
             bf16x8 pb[G][2], dsb[G][2];
@@ -201,15 +210,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
                     }
                 }
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db) {
+                bf16x8 ga[G][2], qa[G][2];
 #pragma unroll
                 for (int u = 0; u < G; ++u)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        const int qc = q0c + u;
-                        dv_acc[db] = mfma_bf16(ld_tr8<D>(gt, qc * 32 + hh * 16, db * 32), pb[u][hh], dv_acc[db]);
-                        dk_acc[db] = mfma_bf16(ld_tr8<D>(qt, qc * 32 + hh * 16, db * 32), dsb[u][hh], dk_acc[db]);
+                        ga[u][hh] = ld_tr8<D>(gt, (q0c + u) * 32 + hh * 16, db * 32);
+                        qa[u][hh] = ld_tr8<D>(qt, (q0c + u) * 32 + hh * 16, db * 32);
                     }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < G; ++u)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        dv_acc[db] = mfma_bf16(ga[u][hh], pb[u][hh], dv_acc[db]);
+                        dk_acc[db] = mfma_bf16(qa[u][hh], dsb[u][hh], dk_acc[db]);
+                    }
+            }
         }
     };
 
@@ -336,11 +354,31 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
         // one 32-key chunk at a time: S^T, dP^T, dS^T, then dQ^T += K^T dS^T
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
+            // operands two k-steps ahead of the products; the group barriers
+            // fix the order (reads for step st+2 right after the MFMAs of st)
             f32x16 s = f32x16{}, dp = f32x16{};
+            constexpr int PF = 2;
+            bf16x8 ka[KSTEPS], va[KSTEPS];
+#pragma unroll
+            for (int st = 0; st < PF; ++st) {
+                ka[st] = ld_row8<D>(kt, kc * 32 + l32, st * 16 + hf * 8);
+                va[st] = ld_row8<D>(vt, kc * 32 + l32, st * 16 + hf * 8);
+            }
 #pragma unroll
             for (int st = 0; st < KSTEPS; ++st) {
-                s = mfma_bf16(ld_row8<D>(kt, kc * 32 + l32, st * 16 + hf * 8), qreg[st], s);
-                dp = mfma_bf16(ld_row8<D>(vt, kc * 32 + l32, st * 16 + hf * 8), greg[st], dp);
+                s = mfma_bf16(ka[st], qreg[st], s);
+                dp = mfma_bf16(va[st], greg[st], dp);
+                if (st + PF < KSTEPS) {
+                    ka[st + PF] = ld_row8<D>(kt, kc * 32 + l32, (st + PF) * 16 + hf * 8);
+                    va[st + PF] = ld_row8<D>(vt, kc * 32 + l32, (st + PF) * 16 + hf * 8);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);      // DS reads
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // MFMA
+                if (st + PF < KSTEPS)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
             }
             bf16x8 dsb[2];
 #pragma unroll
@@ -351,11 +389,18 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
                     pv = 0.f;
                 dsb[i / 8][i % 8] = (bf16)(pv * (dp[i] - dval));
             }
+            bf16x8 kta[NDB][2];
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
-                    dq_acc[db] = mfma_bf16(ld_tr8<D>(kt, kc * 32 + hh * 16, db * 32), dsb[hh], dq_acc[db]);
+                    kta[db][hh] = ld_tr8<D>(kt, kc * 32 + hh * 16, db * 32);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    dq_acc[db] = mfma_bf16(kta[db][hh], dsb[hh], dq_acc[db]);
         }
     };
 

@@ -163,13 +163,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
         if (CAUSAL && kbase > wq0 + 31)
             return;
         // S^T = K_j Q^T
+        // operands first, then the products (keeps LDS latency off each MFMA)
         f32x16 s[NKC];
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
+            bf16x8 ka[KSTEPS];
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st)
+                ka[st] = ld_row8<D>(kt, kc * 32 + l32, st * 16 + hf * 8);
+            __builtin_amdgcn_sched_barrier(0);
             s[kc] = f32x16{};
 #pragma unroll
             for (int st = 0; st < KSTEPS; ++st)
-                s[kc] = mfma_bf16(ld_row8<D>(kt, kc * 32 + l32, st * 16 + hf * 8), qreg[st], s[kc]);
+                s[kc] = mfma_bf16(ka[st], qreg[st], s[kc]);
         }
         // masks: only tiles that cross the diagonal or the key length
         if ((kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0)) {
@@ -214,12 +220,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
         lsum += rs;
         // O^T += V_j^T P^T
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db) {
+            bf16x8 va[NKC][2];
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
-                    oacc[db] = mfma_bf16(ld_tr8<D>(vt, kc * 32 + hh * 16, db * 32), pb[kc][hh], oacc[db]);
+                    va[kc][hh] = ld_tr8<D>(vt, kc * 32 + hh * 16, db * 32);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    oacc[db] = mfma_bf16(va[kc][hh], pb[kc][hh], oacc[db]);
+        }
     };
 
     if (n_tiles > 0)
