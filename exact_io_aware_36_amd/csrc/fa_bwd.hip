@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "fa_tile.h"
 
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
 
     TileDma<BQ, D, 4> dma;
     dma.init(wave);
-    auto issue = [&](int it, bf16 *qd, bf16 *gd, float *ld, float *dd) {
+    auto issue = [&](int it, bf16 *qd, bf16 *gd, float *ld, float *dd) __attribute__((always_inline)) {
         const int qbase = it * BQ;
         dma.issue(qrs, qbase, qd, wave);
         dma.issue(grs, qbase, gd, wave);
@@ -159,11 +161,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
             buffer_to_lds4(drs, dd, lane * 4, qbase * 4);
     };
 
-    auto compute = [&](int it, const bf16 *qt, const bf16 *gt, const float *lt, const float *dt) {
+    // MASKED applies the causal mask.  Only the two query tiles that hold this
+    // workgroup's diagonal (the first two visited, qbase = k0 and k0 + 64)
+    // need it; they are peeled off the main loop below.  Key padding needs no
+    // mask here: a padded key's P reaches only its own dK, dV row, which the
+    // store writes as zero.
+    auto compute = [&](auto masked, int it, const bf16 *qt, const bf16 *gt, const float *lt,
+                       const float *dt) __attribute__((always_inline)) {
         const int qbase = it * BQ;
         if (!wave_live || (CAUSAL && qbase + BQ - 1 < wk0))
             return;
-        const bool need_mask = (CAUSAL && qbase < wk0 + 31) || (wk0 + 32 > kv_len);
+        const bool need_mask = decltype(masked)::value && qbase < wk0 + 31;
         // G 32-query chunks at a time (G = 1 at d = 64 keeps the kernel within
         // 256 registers for two waves per SIMD; G = 2 at d = 128, where the
         // kernel runs one wave per SIMD and more independent MFMA chains pay):
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
                     for (int e = 0; e < 4; ++e) {
                         const int i = 4 * g + e;
                         float pv = exp2_hw(fmaf(s[u][i], c_log2, -l4[e]));
-                        if (need_mask && (key >= kv_len || (CAUSAL && key > qbase + trow + e)))
+                        if (need_mask && key > qbase + trow + e)
                             pv = 0.f;
                         pb[u][i / 8][i % 8] = (bf16)pv;
                         dsb[u][i / 8][i % 8] = (bf16)(pv * (dp[u][i] - d4[e]));
@@ -231,26 +239,38 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         }
     };
 
+    // one step = two query tiles, one per LDS stage
+    auto step = [&](auto masked, int it) __attribute__((always_inline)) {
+        if (it + 1 < qt_end)
+            issue(it + 1, q1s, g1s, l1s, d1s);
+        compute(masked, it, q0s, g0s, l0s, d0s);
+        wait_vmem();
+        __syncthreads();
+        if (it + 1 < qt_end) {
+            if (it + 2 < qt_end)
+                issue(it + 2, q0s, g0s, l0s, d0s);
+            compute(masked, it + 1, q1s, g1s, l1s, d1s);
+            wait_vmem();
+            __syncthreads();
+        }
+    };
     if (qt_begin < qt_end)
         issue(qt_begin, q0s, g0s, l0s, d0s);
     wait_vmem();
     __syncthreads();
-    for (int it = qt_begin; it < qt_end; it += 2) {
-        if (it + 1 < qt_end)
-            issue(it + 1, q1s, g1s, l1s, d1s);
-        compute(it, q0s, g0s, l0s, d0s);
-        wait_vmem();
-        __syncthreads();
-        if (it + 1 >= qt_end)
-            break;
-        if (it + 2 < qt_end)
-            issue(it + 2, q0s, g0s, l0s, d0s);
-        compute(it + 1, q1s, g1s, l1s, d1s);
-        wait_vmem();
-        __syncthreads();
-    }
+    if (qt_begin < qt_end)
+        step(std::integral_constant<bool, CAUSAL>{}, qt_begin);   // the diagonal tiles
+    for (int it = qt_begin + 2; it < qt_end; it += 2)
+        step(std::false_type{}, it);
 
-    // dK = scale * dS^T Q, dV = P^T dO; rows of padded keys stay 0
+    // dK = scale * dS^T Q, dV = P^T dO; rows of padded keys are 0
+    if (key >= kv_len) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            dk_acc[db] = f32x16{};
+            dv_acc[db] = f32x16{};
+        }
+    }
     if (key < N) {
         bf16 *dK = (bf16 *)p.dk + head_off + (size_t)key * D;
         bf16 *dV = (bf16 *)p.dv + head_off + (size_t)key * D;
@@ -341,12 +361,12 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
 
     TileDma<BC, D, 4> dma;
     dma.init(wave);
-    auto issue = [&](int t, bf16 *kd, bf16 *vd) {
+    auto issue = [&](int t, bf16 *kd, bf16 *vd) __attribute__((always_inline)) {
         dma.issue(krs, t * BC, kd, wave);
         dma.issue(vrs, t * BC, vd, wave);
     };
 
-    auto compute = [&](int t, const bf16 *kt, const bf16 *vt) {
+    auto compute = [&](int t, const bf16 *kt, const bf16 *vt) __attribute__((always_inline)) {
         const int kbase = t * BC;
         if (CAUSAL && kbase > wq0 + 31)
             return;

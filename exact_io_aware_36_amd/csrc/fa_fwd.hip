@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
             kv_end = min(kv_end, q0 + BR);
         n_tiles = (kv_end + BC - 1) / BC;
     }
-    auto tile_of = [&](int t) -> int {
+    auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
         if constexpr (SPARSE)
             return __builtin_amdgcn_readfirstlane(blist[t / TPB]) * TPB + t % TPB;
         else
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
 
     TileDma<BC, D, 4> dma;
     dma.init(wave);
-    auto issue = [&](int j, bf16 *kd, bf16 *vd) {
+    auto issue = [&](int j, bf16 *kd, bf16 *vd) __attribute__((always_inline)) {
         dma.issue(krs, j * BC, kd, wave);
         dma.issue(vrs, j * BC, vd, wave);
     };
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
     for (int db = 0; db < NDB; ++db)
         oacc[db] = f32x16{};
 
-    auto compute = [&](int j, const bf16 *kt, const bf16 *vt) {
+    auto compute = [&](int j, const bf16 *kt, const bf16 *vt) __attribute__((always_inline)) {
         const int kbase = j * BC;
         // whole tile above this wave's diagonal: nothing to add
         if (CAUSAL && kbase > wq0 + 31)
