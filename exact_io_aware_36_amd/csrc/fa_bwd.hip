@@ -366,11 +366,14 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
         dma.issue(vrs, t * BC, vd, wave);
     };
 
-    auto compute = [&](int t, const bf16 *kt, const bf16 *vt) __attribute__((always_inline)) {
+    // MASKED instances handle the trailing tiles that cross the causal
+    // diagonal or the key length; the main loop runs the unmasked instance
+    auto compute = [&](auto masked, int t, const bf16 *kt, const bf16 *vt) __attribute__((always_inline)) {
         const int kbase = t * BC;
         if (CAUSAL && kbase > wq0 + 31)
             return;
-        const bool need_mask = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
+        const bool need_mask =
+            decltype(masked)::value && ((kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0));
         // one 32-key chunk at a time: S^T, dP^T, dS^T, then dQ^T += K^T dS^T
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
@@ -424,24 +427,33 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
         }
     };
 
+    auto step = [&](auto masked, int t) __attribute__((always_inline)) {
+        if (t + 1 < n_tiles)
+            issue(t + 1, k1s, v1s);
+        compute(masked, t, k0s, v0s);
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 < n_tiles) {
+            if (t + 2 < n_tiles)
+                issue(t + 2, k0s, v0s);
+            compute(masked, t + 1, k1s, v1s);
+            wait_vmem();
+            __syncthreads();
+        }
+    };
+    // leading tiles that no wave needs to mask
+    int n_plain = min(n_tiles, kv_len / BC);
+    if (CAUSAL)
+        n_plain = min(n_plain, (q0 + 1) / BC);
+    const int t_mask = n_plain & ~1;
     if (n_tiles > 0)
         issue(0, k0s, v0s);
     wait_vmem();
     __syncthreads();
-    for (int t = 0; t < n_tiles; t += 2) {
-        if (t + 1 < n_tiles)
-            issue(t + 1, k1s, v1s);
-        compute(t, k0s, v0s);
-        wait_vmem();
-        __syncthreads();
-        if (t + 1 >= n_tiles)
-            break;
-        if (t + 2 < n_tiles)
-            issue(t + 2, k0s, v0s);
-        compute(t + 1, k1s, v1s);
-        wait_vmem();
-        __syncthreads();
-    }
+    for (int t = 0; t < t_mask; t += 2)
+        step(std::false_type{}, t);
+    for (int t = t_mask; t < n_tiles; t += 2)
+        step(std::true_type{}, t);
 
     if (qrow < N) {
         bf16 *dQ = (bf16 *)p.dq + head_off + (size_t)qrow * D;

@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "fa_tile.h"
 
@@ -157,7 +159,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
     for (int db = 0; db < NDB; ++db)
         oacc[db] = f32x16{};
 
-    auto compute = [&](int j, const bf16 *kt, const bf16 *vt) __attribute__((always_inline)) {
+    // MASKED instances handle the trailing tiles that cross the causal
+    // diagonal or the key length; the main loop runs the unmasked instance
+    auto compute = [&](auto masked, int j, const bf16 *kt, const bf16 *vt) __attribute__((always_inline)) {
         const int kbase = j * BC;
         // whole tile above this wave's diagonal: nothing to add
         if (CAUSAL && kbase > wq0 + 31)
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
                 s[kc] = mfma_bf16(ka[st], qreg[st], s[kc]);
         }
         // masks: only tiles that cross the diagonal or the key length
-        if ((kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0)) {
+        if (decltype(masked)::value && ((kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0))) {
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
@@ -236,24 +240,38 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
         }
     };
 
+    // one step = two tiles, one per LDS stage
+    auto step = [&](auto masked, int t) __attribute__((always_inline)) {
+        if (t + 1 < n_tiles)
+            issue(tile_of(t + 1), k1s, v1s);
+        compute(masked, tile_of(t), k0s, v0s);
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 < n_tiles) {
+            if (t + 2 < n_tiles)
+                issue(tile_of(t + 2), k0s, v0s);
+            compute(masked, tile_of(t + 1), k1s, v1s);
+            wait_vmem();
+            __syncthreads();
+        }
+    };
+    // leading tiles that no wave needs to mask: whole tiles below the key
+    // length and (causal) entirely at or left of the block's first query
+    int n_plain = n_tiles;
+    if constexpr (!SPARSE) {
+        n_plain = min(n_tiles, kv_len / BC);
+        if (CAUSAL)
+            n_plain = min(n_plain, (q0 + 1) / BC);
+    }
+    const int t_mask = n_plain & ~1;
     if (n_tiles > 0)
         issue(tile_of(0), k0s, v0s);
     wait_vmem();
     __syncthreads();
-    for (int t = 0; t < n_tiles; t += 2) {
-        if (t + 1 < n_tiles)
-            issue(tile_of(t + 1), k1s, v1s);
-        compute(tile_of(t), k0s, v0s);
-        wait_vmem();
-        __syncthreads();
-        if (t + 1 >= n_tiles)
-            break;
-        if (t + 2 < n_tiles)
-            issue(tile_of(t + 2), k0s, v0s);
-        compute(tile_of(t + 1), k1s, v1s);
-        wait_vmem();
-        __syncthreads();
-    }
+    for (int t = 0; t < t_mask; t += 2)
+        step(std::false_type{}, t);
+    for (int t = t_mask; t < n_tiles; t += 2)
+        step(std::true_type{}, t);
 
     // ---- epilogue: O = acc / l, LSE = ln2 (m + log2 l)
     const float ltot = pair_sum(lsum);
