@@ -159,19 +159,23 @@ def cpu_baseline(inp, w, metric_flops, budget_s=15.0, seed=99):
                                   scale=w.scale, kv_len=None if lens is None else int(lens[b]),
                                   block_mask=mask, mask_block=w.mask_block)
 
-    probe = np.sort(rng.choice(total_rows, min(64, total_rows), replace=False))
-    t0 = time.perf_counter()
-    run(probe)
-    t_probe = max(time.perf_counter() - t0, 1e-3)
-    n = int(min(total_rows, max(64, len(probe) * budget_s / t_probe)))
-    rows = np.sort(rng.choice(total_rows, n, replace=False))
-    t0 = time.perf_counter()
-    run(rows)
-    dt = time.perf_counter() - t0
+    # batches of random rows (doubling) until the budget is spent
+    done = 0
+    dt = 0.0
+    batch = 64
+    while dt < budget_s and done < total_rows:
+        rows = np.sort(rng.choice(total_rows, min(batch, total_rows - done), replace=False))
+        t0 = time.perf_counter()
+        run(rows)
+        dt += time.perf_counter() - t0
+        done += rows.size
+        batch *= 2
+    n = done
     flops = metric_flops * n / total_rows
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-        "sample": (f"{n} of {total_rows} query rows drawn uniformly at random: oracle fp64 forward "
+        "sample": (f"{n} of {total_rows} query rows drawn uniformly at random (batches of 64, 128, "
+                   f"... until {budget_s:.0f} s): oracle fp64 forward "
                    f"rows{' + backward dQ rows' if w.backward else ''}, {dt:.1f} s; credited "
                    f"{n}/{total_rows} of one step's {metric_flops:.4g} flops"),
         "seconds": dt,
