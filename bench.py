@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "bwd_dot": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
     "bwd_dkdv": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
     "bwd_dq": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
+    "bwd_sparse": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
 }
 
 
@@ -72,7 +73,8 @@ def kernel_flops(stage, B, H, N, d, causal=False, sparse_frac=None) -> float:
     two products per (query, allowed key) pair (S and P V), the dK/dV kernel
     four (S, dP, dV, dK), the dQ kernel three (S, dP, dQ); 2 d flops each."""
     f = fwd_flops(B, H, N, d, causal, sparse_frac)
-    return {"fwd": f, "bwd_dkdv": 2.0 * f, "bwd_dq": 1.5 * f, "bwd_dot": 0.0}[stage]
+    return {"fwd": f, "bwd_dkdv": 2.0 * f, "bwd_dq": 1.5 * f, "bwd_dot": 0.0,
+            "bwd_sparse": 3.5 * f}[stage]
 
 
 def floor_bytes(stage, B, H, N, d, elem=2) -> float:
@@ -84,6 +86,7 @@ def floor_bytes(stage, B, H, N, d, elem=2) -> float:
         "bwd_dot": 2 * t + 3 * rows,         # O, dO, LSE in; D, LSE*log2e out
         "bwd_dkdv": 6 * t + 2 * rows,        # Q, K, V, dO, LSE*log2e, D in; dK, dV out
         "bwd_dq": 5 * t + 2 * rows,          # Q, K, V, dO, LSE*log2e, D in; dQ out
+        "bwd_sparse": 8 * t + 4 * rows,      # the three launches of the sparse backward
     }[stage]
 
 
@@ -227,7 +230,12 @@ def main(argv=None):
         ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    stages = ["fwd"] + (["bwd_dot", "bwd_dkdv", "bwd_dq"] if w.backward else [])
+    if not w.backward:
+        stages = ["fwd"]
+    elif mask is None:
+        stages = ["fwd", "bwd_dot", "bwd_dkdv", "bwd_dq"]
+    else:
+        stages = ["fwd", "bwd_sparse"]     # fa_bwd_blocksparse: its three launches together
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -252,6 +260,9 @@ def main(argv=None):
                            kv_lens=lens)
         elif stage == "bwd_dq":
             fa.fa_bwd_dq(q, k, v, dout, lse, dq, ws, causal=w.causal, scale=w.scale, kv_lens=lens)
+        elif stage == "bwd_sparse":
+            fa.fa_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, ws, mask,
+                                  mask_block=w.mask_block, scale=w.scale)
 
     for _ in range(args.warmup):
         for s in stages:

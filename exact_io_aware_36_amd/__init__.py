@@ -3,10 +3,12 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/fa.h.  The functions named like
 the C entry points (fa_fwd, fa_fwd_ex, fa_bwd, fa_bwd_workspace_bytes,
-fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_fwd_blocksparse, fa_status_str)
+fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_fwd_blocksparse, fa_bwd_blocksparse,
+fa_status_str)
 take torch device tensors, read their shapes and pointers and call the C
-function of the same name on the current torch stream (or the stream given).  fwd, bwd and fwd_blocksparse are the same
-calls with the outputs (and the backward workspace) allocated by torch.
+function of the same name on the current torch stream (or the stream given).  fwd, bwd, fwd_blocksparse and
+bwd_blocksparse are the same calls with the outputs (and the backward
+workspace) allocated by torch.
 
 There is no fallback: importing this package raises if libfa.so has not been
 built, and every call raises FAError on a non-zero status.
@@ -21,8 +23,8 @@ import torch  # loads torch's HIP runtime first, so libfa.so binds to the same o
 
 __all__ = [
     "FAError", "fa_status_str", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_bytes",
-    "fa_fwd_blocksparse", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fwd", "bwd",
-    "fwd_blocksparse", "library_path",
+    "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
+    "fwd", "bwd", "fwd_blocksparse", "bwd_blocksparse", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +76,9 @@ _lib.fa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, 
 _lib.fa_bwd_dq.restype = _i
 _lib.fa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i, _vp, _sz,
                            _vp]
+_lib.fa_bwd_blocksparse.restype = _i
+_lib.fa_bwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,
+                                    _vp, _i, _i, _vp, _sz, _vp]
 _lib.fa_fwd_blocksparse.restype = _i
 _lib.fa_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _i, _vp]
 
@@ -226,6 +231,23 @@ def fa_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_block=128, scale=None, 
     _check_rc(rc, "fa_fwd_blocksparse")
 
 
+def fa_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, workspace, block_mask, mask_block=128,
+                       scale=None, stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, o, dout, dq, dk, dv)
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * N,
+             "lse must be contiguous fp32 [B, H, N]")
+    _require(block_mask.dtype == torch.uint8 and block_mask.is_contiguous(),
+             "block_mask must be contiguous uint8")
+    nb = N // mask_block if mask_block > 0 else 0
+    _require(block_mask.numel() == nb * nb, "block_mask must be [N/mask_block, N/mask_block]")
+    rc = _lib.fa_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), _ptr(block_mask),
+                                 int(mask_block), _dtype(q), _ptr(workspace), _ws_bytes(workspace),
+                                 _stream(q, stream))
+    _check_rc(rc, "fa_bwd_blocksparse")
+
+
 # -- the same calls with torch-allocated outputs ------------------------------
 
 def fwd(q, k, v, causal=False, scale=None, kv_lens=None, tile_n=0, stream=None):
@@ -245,6 +267,16 @@ def bwd(q, k, v, o, dout, lse, causal=False, scale=None, kv_lens=None, stream=No
     ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal=causal, scale=scale, kv_lens=kv_lens,
            stream=stream)
+    return dq, dk, dv
+
+
+def bwd_blocksparse(q, k, v, o, dout, lse, block_mask, mask_block=128, scale=None, stream=None):
+    """Return (dQ, dK, dV) of the block-sparse forward."""
+    B, H, N, d = _shape(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    fa_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, ws, block_mask, mask_block=mask_block,
+                       scale=scale, stream=stream)
     return dq, dk, dv
 
 

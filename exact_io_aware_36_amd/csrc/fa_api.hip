@@ -126,7 +126,7 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
     float *ws = (float *)workspace;
     float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
     fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, ws, ws2, B, H, N, scale, kv_lens};
-    return from_hip(fa::launch_bwd_bf16(a, d, causal != 0, (hipStream_t)stream));
+    return from_hip(fa::launch_bwd_bf16(a, d, causal != 0, false, (hipStream_t)stream));
 }
 
 fa_status fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, int H,
@@ -142,7 +142,7 @@ fa_status fa_bwd_preprocess(const void *o, const void *dout, const float *lse, i
     float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
     fa::BwdArgs a{nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr, ws, ws2,
                   B, H, N, 1.f, nullptr};
-    return from_hip(fa::launch_bwd_stage(a, d, false, fa::BwdStage::Dot, (hipStream_t)stream));
+    return from_hip(fa::launch_bwd_stage(a, d, false, false, fa::BwdStage::Dot, (hipStream_t)stream));
 }
 
 fa_status fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
@@ -157,7 +157,7 @@ fa_status fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *d
     float *ws = (float *)workspace;
     float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
     fa::BwdArgs a{q, k, v, nullptr, dout, lse, nullptr, dk, dv, ws, ws2, B, H, N, scale, kv_lens};
-    return from_hip(fa::launch_bwd_stage(a, d, causal != 0, fa::BwdStage::DkDv, (hipStream_t)stream));
+    return from_hip(fa::launch_bwd_stage(a, d, causal != 0, false, fa::BwdStage::DkDv, (hipStream_t)stream));
 }
 
 fa_status fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
@@ -173,7 +173,7 @@ fa_status fa_bwd_dq(const void *q, const void *k, const void *v, const void *dou
     float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
     fa::BwdArgs a{q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, ws, ws2, B, H, N, scale,
                   kv_lens};
-    return from_hip(fa::launch_bwd_stage(a, d, causal != 0, fa::BwdStage::Dq, (hipStream_t)stream));
+    return from_hip(fa::launch_bwd_stage(a, d, causal != 0, false, fa::BwdStage::Dq, (hipStream_t)stream));
 }
 
 fa_status fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -187,12 +187,33 @@ fa_status fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *
         return FA_ERR_INVALID_ARG;
     if (mask_block != 128 || N % mask_block != 0)
         return FA_ERR_INVALID_ARG;
-    if (N / mask_block > 512)
+    if (N / mask_block > fa::MAX_MASK_BLOCKS)
         return FA_ERR_UNSUPPORTED;
     if (dtype != FA_DTYPE_BF16)
         return FA_ERR_UNSUPPORTED;
     fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale, nullptr, block_mask, N / mask_block};
     return from_hip(fa::launch_fwd_bf16(a, d, 0, false, true, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_blocksparse(const void *q, const void *k, const void *v, const void *o,
+                             const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                             int B, int H, int N, int d, float scale, const uint8_t *block_mask,
+                             int mask_block, fa_dtype dtype, void *workspace,
+                             size_t workspace_bytes, fa_stream_t stream)
+{
+    fa_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, nullptr, dtype,
+                             workspace, workspace_bytes);
+    if (st != FA_OK)
+        return st;
+    if (!block_mask || mask_block != 128 || N % mask_block != 0)
+        return FA_ERR_INVALID_ARG;
+    if (N / mask_block > fa::MAX_MASK_BLOCKS)
+        return FA_ERR_UNSUPPORTED;
+    float *ws = (float *)workspace;
+    float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, ws, ws2, B, H, N, scale, nullptr,
+                  block_mask, N / mask_block};
+    return from_hip(fa::launch_bwd_bf16(a, d, false, true, (hipStream_t)stream));
 }
 
 } // extern "C"

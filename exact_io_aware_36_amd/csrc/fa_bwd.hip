@@ -20,6 +20,10 @@
 //      query tiles, accumulating dK and dV in registers.
 //   3. bwd_dq_kernel: queries outer.  A workgroup owns 128 queries and walks
 //      the key tiles, accumulating dQ in registers.
+// Block-sparse instances walk only the nonzero blocks of the mask: the
+// dK/dV workgroup's 128 keys are one mask column block (it visits the query
+// tiles of that column's nonzero row blocks), the dQ workgroup's 128 queries
+// one mask row block (the key tiles of that row's nonzero column blocks).
 // No atomics: every output element is written by exactly one lane, so the
 // result is deterministic.
 //
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16 *__restrict__ o
 // Q and dO tiles (and their rows' LSE and D) reach LDS by direct buffer->LDS
 // loads into two stages; the loop is unrolled by two.  Query rows past N read
 // as zeros (Q, dO, LSE, D all 0), which makes their dS and P^T dO terms 0.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs p, float c_log2)
 {
     constexpr int BKV = 128, BQ = 64;
@@ -144,9 +148,28 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         dv_acc[db] = f32x16{};
     }
 
+    // the query tiles visited, in order: dense, all tiles from the diagonal
+    // (causal) or from 0; block-sparse, the two tiles of every nonzero row
+    // block of this key block's mask column
+    __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
+    __shared__ int bcount;
     const int n_qt = (N + BQ - 1) / BQ;
     const int qt_begin = (CAUSAL ? k0 / BQ : 0);
-    const int qt_end = (k0 < kv_len) ? n_qt : qt_begin;   // no allowed key: nothing to do
+    int n_vis;
+    if constexpr (SPARSE) {
+        if (wave == 0)
+            list_nonzero(p.mask + kb, p.nb, p.nb, blist, &bcount);
+        __syncthreads();
+        n_vis = __builtin_amdgcn_readfirstlane(bcount) * (128 / BQ);
+    } else {
+        n_vis = (k0 < kv_len) ? n_qt - qt_begin : 0;   // no allowed key: nothing to do
+    }
+    auto qtile = [&](int t) __attribute__((always_inline)) -> int {
+        if constexpr (SPARSE)
+            return __builtin_amdgcn_readfirstlane(blist[t / (128 / BQ)]) * (128 / BQ) + t % (128 / BQ);
+        else
+            return qt_begin + t;
+    };
     const bool wave_live = wk0 < kv_len;
 
     TileDma<BQ, D, 4> dma;
@@ -239,29 +262,29 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         }
     };
 
-    // one step = two query tiles, one per LDS stage
-    auto step = [&](auto masked, int it) __attribute__((always_inline)) {
-        if (it + 1 < qt_end)
-            issue(it + 1, q1s, g1s, l1s, d1s);
-        compute(masked, it, q0s, g0s, l0s, d0s);
+    // one step = two visited query tiles, one per LDS stage
+    auto step = [&](auto masked, int t) __attribute__((always_inline)) {
+        if (t + 1 < n_vis)
+            issue(qtile(t + 1), q1s, g1s, l1s, d1s);
+        compute(masked, qtile(t), q0s, g0s, l0s, d0s);
         wait_vmem();
         __syncthreads();
-        if (it + 1 < qt_end) {
-            if (it + 2 < qt_end)
-                issue(it + 2, q0s, g0s, l0s, d0s);
-            compute(masked, it + 1, q1s, g1s, l1s, d1s);
+        if (t + 1 < n_vis) {
+            if (t + 2 < n_vis)
+                issue(qtile(t + 2), q0s, g0s, l0s, d0s);
+            compute(masked, qtile(t + 1), q1s, g1s, l1s, d1s);
             wait_vmem();
             __syncthreads();
         }
     };
-    if (qt_begin < qt_end)
-        issue(qt_begin, q0s, g0s, l0s, d0s);
+    if (n_vis > 0)
+        issue(qtile(0), q0s, g0s, l0s, d0s);
     wait_vmem();
     __syncthreads();
-    if (qt_begin < qt_end)
-        step(std::integral_constant<bool, CAUSAL>{}, qt_begin);   // the diagonal tiles
-    for (int it = qt_begin + 2; it < qt_end; it += 2)
-        step(std::false_type{}, it);
+    if (n_vis > 0)
+        step(std::integral_constant<bool, CAUSAL>{}, 0);   // the diagonal tiles (causal)
+    for (int t = 2; t < n_vis; t += 2)
+        step(std::false_type{}, t);
 
     // dK = scale * dS^T Q, dV = P^T dO; rows of padded keys are 0
     if (key >= kv_len) {
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
 
 // dQ: queries outer ---------------------------------------------------------
 // K and V tiles reach LDS by direct buffer->LDS loads into two stages.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_kernel(BwdArgs p, float c_log2)
 {
     constexpr int BR = 128, BC = 64;
@@ -354,22 +377,41 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
     for (int db = 0; db < NDB; ++db)
         dq_acc[db] = f32x16{};
 
-    int kv_end = kv_len;
-    if (CAUSAL)
-        kv_end = min(kv_end, q0 + BR);
-    const int n_tiles = (kv_end + BC - 1) / BC;
+    // the key tiles visited: dense, 0 .. up to the diagonal / key length;
+    // block-sparse, the two tiles of every nonzero block of this query
+    // block's mask row
+    __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
+    __shared__ int bcount;
+    int n_tiles;
+    if constexpr (SPARSE) {
+        if (wave == 0)
+            list_nonzero(p.mask + (size_t)qb * p.nb, p.nb, 1, blist, &bcount);
+        __syncthreads();
+        n_tiles = __builtin_amdgcn_readfirstlane(bcount) * (128 / BC);
+    } else {
+        int kv_end = kv_len;
+        if (CAUSAL)
+            kv_end = min(kv_end, q0 + BR);
+        n_tiles = (kv_end + BC - 1) / BC;
+    }
+    auto ktile = [&](int t) __attribute__((always_inline)) -> int {
+        if constexpr (SPARSE)
+            return __builtin_amdgcn_readfirstlane(blist[t / (128 / BC)]) * (128 / BC) + t % (128 / BC);
+        else
+            return t;
+    };
 
     TileDma<BC, D, 4> dma;
     dma.init(wave);
     auto issue = [&](int t, bf16 *kd, bf16 *vd) __attribute__((always_inline)) {
-        dma.issue(krs, t * BC, kd, wave);
-        dma.issue(vrs, t * BC, vd, wave);
+        dma.issue(krs, ktile(t) * BC, kd, wave);
+        dma.issue(vrs, ktile(t) * BC, vd, wave);
     };
 
     // MASKED instances handle the trailing tiles that cross the causal
     // diagonal or the key length; the main loop runs the unmasked instance
     auto compute = [&](auto masked, int t, const bf16 *kt, const bf16 *vt) __attribute__((always_inline)) {
-        const int kbase = t * BC;
+        const int kbase = ktile(t) * BC;
         if (CAUSAL && kbase > wq0 + 31)
             return;
         const bool need_mask =
@@ -442,9 +484,12 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
         }
     };
     // leading tiles that no wave needs to mask
-    int n_plain = min(n_tiles, kv_len / BC);
-    if (CAUSAL)
-        n_plain = min(n_plain, (q0 + 1) / BC);
+    int n_plain = n_tiles;
+    if constexpr (!SPARSE) {
+        n_plain = min(n_tiles, kv_len / BC);
+        if (CAUSAL)
+            n_plain = min(n_plain, (q0 + 1) / BC);
+    }
     const int t_mask = n_plain & ~1;
     if (n_tiles > 0)
         issue(0, k0s, v0s);
@@ -483,56 +528,65 @@ hipError_t launch_dot(const BwdArgs &a, hipStream_t s)
                            kargs, 0, s);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_dkdv(const BwdArgs &a, hipStream_t s)
 {
     BwdArgs args = a;
     float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     const int n_kb = (a.N + 127) / 128;
-    return hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, CAUSAL>, dim3(a.B * a.H * n_kb),
+    return hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, CAUSAL, SPARSE>, dim3(a.B * a.H * n_kb),
                            dim3(256), kargs, 0, s);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_dq(const BwdArgs &a, hipStream_t s)
 {
     BwdArgs args = a;
     float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     const int n_qb = (a.N + 127) / 128;
-    return hipLaunchKernel((const void *)&bwd_dq_kernel<D, CAUSAL>, dim3(a.B * a.H * n_qb),
+    return hipLaunchKernel((const void *)&bwd_dq_kernel<D, CAUSAL, SPARSE>, dim3(a.B * a.H * n_qb),
                            dim3(256), kargs, 0, s);
 }
 
-} // namespace
-
-hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, BwdStage stage, hipStream_t s)
+template <int D>
+hipError_t launch_d(const BwdArgs &a, bool causal, bool sparse, BwdStage stage, hipStream_t s)
 {
-    if (d != 64 && d != 128)
-        return hipErrorInvalidValue;
     switch (stage) {
     case BwdStage::Dot:
-        return d == 64 ? launch_dot<64>(a, s) : launch_dot<128>(a, s);
+        return launch_dot<D>(a, s);
     case BwdStage::DkDv:
-        if (d == 64)
-            return causal ? launch_dkdv<64, true>(a, s) : launch_dkdv<64, false>(a, s);
-        return causal ? launch_dkdv<128, true>(a, s) : launch_dkdv<128, false>(a, s);
+        if (sparse)
+            return launch_dkdv<D, false, true>(a, s);
+        return causal ? launch_dkdv<D, true, false>(a, s) : launch_dkdv<D, false, false>(a, s);
     case BwdStage::Dq:
-        if (d == 64)
-            return causal ? launch_dq<64, true>(a, s) : launch_dq<64, false>(a, s);
-        return causal ? launch_dq<128, true>(a, s) : launch_dq<128, false>(a, s);
+        if (sparse)
+            return launch_dq<D, false, true>(a, s);
+        return causal ? launch_dq<D, true, false>(a, s) : launch_dq<D, false, false>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, hipStream_t s)
+} // namespace
+
+hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, bool sparse, BwdStage stage,
+                            hipStream_t s)
 {
-    hipError_t e = launch_bwd_stage(a, d, causal, BwdStage::Dot, s);
+    if (d == 64)
+        return launch_d<64>(a, causal, sparse, stage, s);
+    if (d == 128)
+        return launch_d<128>(a, causal, sparse, stage, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, bool sparse, hipStream_t s)
+{
+    hipError_t e = launch_bwd_stage(a, d, causal, sparse, BwdStage::Dot, s);
     if (e == hipSuccess)
-        e = launch_bwd_stage(a, d, causal, BwdStage::DkDv, s);
+        e = launch_bwd_stage(a, d, causal, sparse, BwdStage::DkDv, s);
     if (e == hipSuccess)
-        e = launch_bwd_stage(a, d, causal, BwdStage::Dq, s);
+        e = launch_bwd_stage(a, d, causal, sparse, BwdStage::Dq, s);
     return e;
 }
 

@@ -49,7 +49,6 @@
 
 namespace fa {
 
-constexpr int MAX_MASK_BLOCKS = 512;   // sparse: N <= 65536 with 128-blocks
 constexpr float TAU = 8.f;             // lazy-rescale threshold (log2 units)
 
 // ---------------------------------------------------------------------------
@@ -105,21 +104,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log
     int n_tiles;
     constexpr int TPB = 128 / BC;            // tiles per 128-block (sparse)
     if constexpr (SPARSE) {
-        if (wave == 0) {
-            const uint8_t *mrow = p.mask + (size_t)qb * p.nb;
-            int cnt = 0;
-            for (int base = 0; base < p.nb; base += 64) {
-                const int c = base + lane;
-                const bool on = c < p.nb && mrow[c] != 0;
-                const unsigned long long bits = __ballot(on);
-                const int pos = cnt + __popcll(bits & ((1ull << lane) - 1ull));
-                if (on)
-                    blist[pos] = c;
-                cnt += __popcll(bits);
-            }
-            if (lane == 0)
-                bcount = cnt;
-        }
+        if (wave == 0)
+            list_nonzero(p.mask + (size_t)qb * p.nb, p.nb, 1, blist, &bcount);
         __syncthreads();
         n_tiles = __builtin_amdgcn_readfirstlane(bcount) * TPB;
     } else {

@@ -28,15 +28,41 @@ struct BwdArgs {
     int B, H, N;
     float scale;
     const int32_t *kv_lens;
+    const uint8_t *mask;    // block mask (sparse launches only)
+    int nb;                 // mask blocks per side (sparse launches only)
 };
 
 // Kernel launchers; each returns the launch status and enqueues only.
 hipError_t launch_fwd_bf16(const FwdArgs &a, int d, int tile_n, bool causal, bool sparse,
                            hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, bool sparse, hipStream_t s);
 enum class BwdStage { Dot, DkDv, Dq };
-hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, BwdStage stage, hipStream_t s);
+hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, bool sparse, BwdStage stage,
+                            hipStream_t s);
+
+constexpr int MAX_MASK_BLOCKS = 512;   // block-sparse: N <= 65536 with 128-blocks
+
+// Wave 0 of the workgroup lists, in increasing order, the indices i < n with
+// mask[i * stride] != 0 into list[] (LDS) and their count into *count; the
+// caller synchronises the workgroup before reading them.
+__device__ __forceinline__ void list_nonzero(const uint8_t *mask, int n, int stride, int *list,
+                                             int *count)
+{
+    const int lane = threadIdx.x & 63;
+    int cnt = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int i = base + lane;
+        const bool on = i < n && mask[(size_t)i * stride] != 0;
+        const unsigned long long bits = __ballot(on);
+        const int pos = cnt + __popcll(bits & ((1ull << lane) - 1ull));
+        if (on)
+            list[pos] = i;
+        cnt += __popcll(bits);
+    }
+    if (lane == 0)
+        *count = cnt;
+}
 
 // The workgroup-to-tile remap used by every attention grid: workgroups are
 // dispatched round-robin over the 8 XCDs, so work item w is given to the

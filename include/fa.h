@@ -178,6 +178,25 @@ fa_status fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *
                              const uint8_t *block_mask, int mask_block, fa_dtype dtype,
                              fa_stream_t stream);
 
+/*
+ * Block-sparse backward: dQ, dK, dV of the block-sparse forward above (same
+ * mask, same conventions), with S and P recomputed only on the tiles of
+ * nonzero blocks -- the training-side counterpart of the block-sparse
+ * paragraph of "Attention" (learn-kernels.com).  The keys of a zero block
+ * get no gradient from that block's queries; a key whose mask column is
+ * all zero gets dK = dV = 0.
+ *   q, k, v, o, dout, lse   as for fa_bwd (lse from fa_fwd_blocksparse with
+ *                           the same mask)
+ *   block_mask, mask_block  as for fa_fwd_blocksparse
+ *   workspace               as for fa_bwd (fa_bwd_workspace_bytes bytes)
+ * Errors: as fa_bwd and fa_fwd_blocksparse.
+ */
+fa_status fa_bwd_blocksparse(const void *q, const void *k, const void *v, const void *o,
+                             const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                             int B, int H, int N, int d, float scale,
+                             const uint8_t *block_mask, int mask_block, fa_dtype dtype,
+                             void *workspace, size_t workspace_bytes, fa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -159,3 +159,21 @@ def test_library_has_no_unresolved_kernels():
     out = subprocess.run([nm, "-u", fa.library_path], capture_output=True, text=True).stdout
     bad = [ln for ln in out.splitlines() if "_ZN2fa" in ln]
     assert not bad, bad
+
+
+def bwd_sparse(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=1, N=256, d=64,
+               scale=0.125, mask=P, mb=128, dtype=BF16, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    return lib.fa_bwd_blocksparse(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, scale, mask, mb,
+                                  dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(mask=None), INVALID), (dict(mb=64), INVALID), (dict(N=200), INVALID),
+    (dict(N=131072), UNSUPPORTED), (dict(dtype=FP32), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(dq=None), INVALID), (dict(lse=None), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(ws_bytes=8), WORKSPACE), (dict(scale=0.0), INVALID),
+])
+def test_bwd_sparse_rejects(lib, kw, want):
+    assert bwd_sparse(lib, **kw) == want

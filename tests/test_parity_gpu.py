@@ -194,6 +194,44 @@ def test_blocksparse_empty_row_and_full_mask(fa):
 
 
 # ---------------------------------------------------------------------------
+# block-sparse backward
+
+@pytest.mark.parametrize("N,d,mask", [
+    (512, 64, "random25"), (384, 128, "random50"), (384, 64, "holes"), (256, 128, "ones")])
+def test_blocksparse_bwd_small(fa, N, d, mask):
+    say(f"  sparse bwd N={N} d={d} mask={mask}")
+    inp = workloads.random_qkv(2, 2, N, d, seed=N + d + 7)
+    nb = N // 128
+    if mask == "random25":
+        m = workloads.random_block_mask(nb, 0.25, seed=1)
+    elif mask == "random50":
+        m = workloads.random_block_mask(nb, 0.5, seed=2)
+    elif mask == "holes":
+        # row 1 empty (its queries see nothing), column 2 empty (its keys get no gradient)
+        m = torch.tensor([[1, 0, 0], [0, 0, 0], [1, 1, 0]], dtype=torch.uint8)
+    else:
+        m = torch.ones(nb, nb, dtype=torch.uint8)
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["dout"])
+    dm = dev(m)
+    o, lse = fa.fwd_blocksparse(q, k, v, dm)
+    dq, dk, dv = fa.bwd_blocksparse(q, k, v, o, do, lse, dm)
+    torch.cuda.synchronize()
+    dQ, dK, dV, _ = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["dout"]),
+                               block_mask=m.numpy(), mask_block=128)
+    check_bf16("dQ", host(dq), dQ)
+    check_bf16("dK", host(dk), dK)
+    check_bf16("dV", host(dv), dV)
+    if mask == "holes":
+        assert (host(dq)[:, :, 128:256] == 0).all()
+        assert (host(dk)[:, :, 256:] == 0).all() and (host(dv)[:, :, 256:] == 0).all()
+    if mask == "ones":
+        r = fa.bwd(q, k, v, o, do, lse)
+        torch.cuda.synchronize()
+        for a, b in zip((dq, dk, dv), r):
+            assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
 # backward, small shapes
 
 @pytest.mark.parametrize("shape", [(2, 2, 300, 64), (1, 2, 257, 128), (1, 1, 64, 64),
@@ -321,6 +359,32 @@ def test_workload_long_context_tiles(fa, tile_n):
                              scale=w.scale)
     check_bf16(f"O[rows] tile={tile_n}", host(o).reshape(-1, w.d)[rows], Or)
     check_lse("LSE[rows]", host(lse).reshape(-1)[rows], Lr)
+
+
+def test_workload_block_sparse_backward(fa):
+    """The block-sparse workload with a backward pass (dO drawn after Q, K,
+    V from the same seed): the oracle checks dQ on 64 query rows and dK, dV on
+    64 key rows of two heads."""
+    w = workloads.WORKLOADS["block_sparse_fwdbwd"]
+    inp = workloads.make_inputs(w)
+    say(f"  {w.name}")
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["dout"])
+    mask = inp["block_mask"]
+    dm = dev(mask)
+    o, lse = fa.fwd_blocksparse(q, k, v, dm)
+    dq, dk, dv = fa.bwd_blocksparse(q, k, v, o, do, lse, dm)
+    torch.cuda.synchronize()
+    B, H, N, d = q.shape
+    rng = np.random.default_rng(5)
+    qf, kf, vf, dof = (f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        qr = np.concatenate([[0, N - 1], rng.choice(N, 62, replace=False)])
+        kr = np.concatenate([[0, N - 1], rng.choice(N, 62, replace=False)])
+        sq, sk, sv = oracle.bwd_sample(qf[b, h], kf[b, h], vf[b, h], dof[b, h], qr, kr,
+                                       scale=w.scale, block_mask=mask.numpy(), mask_block=128)
+        check_bf16(f"dQ[{b},{h}]", host(dq)[b, h, qr], sq)
+        check_bf16(f"dK[{b},{h}]", host(dk)[b, h, kr], sk)
+        check_bf16(f"dV[{b},{h}]", host(dv)[b, h, kr], sv)
 
 
 def test_workload_block_sparse(fa):

@@ -56,6 +56,10 @@ WORKLOADS = {
     "block_sparse": Workload("block_sparse", 4, 16, 4096, 64, "bf16", False, 1005,
                              sparse_frac=0.25,
                              note="block-sparse forward, 128x128 blocks, s=0.25"),
+    # the same block-sparse shape with a backward pass (training-side use)
+    "block_sparse_fwdbwd": Workload("block_sparse_fwdbwd", 4, 16, 4096, 64, "bf16", False, 1005,
+                                    sparse_frac=0.25, backward=True,
+                                    note="block-sparse forward + backward, s=0.25"),
 }
 
 
