@@ -105,9 +105,17 @@ def flash_io_elements(N, d, M) -> float:
 
 # ---------------------------------------------------------------------------
 
+KERNEL_HEADERS = ("exact_io_aware_36_amd/csrc/fa_tile.h", "exact_io_aware_36_amd/csrc/fa_internal.h")
+
+
 def source_digest(path: str) -> str:
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 over the kernel source followed by the
+    two headers every kernel includes."""
+    h = hashlib.sha256()
+    for p in (path,) + KERNEL_HEADERS:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(stage: str, workload: str):

@@ -60,6 +60,12 @@ def _load():
                                          ctypes.c_int, ctypes.c_double, ctypes.c_int, _u8p,
                                          ctypes.c_int, _i64p, ctypes.c_int64, _dp, _i64p,
                                          ctypes.c_int64, _dp, _dp]
+    lib.fa_oracle_decode.restype = ctypes.c_int
+    lib.fa_oracle_decode.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_double, _i32p]
+    lib.fa_oracle_merge.restype = ctypes.c_int
+    lib.fa_oracle_merge.argtypes = [_dp, _dp, ctypes.c_int, ctypes.c_int64, ctypes.c_int, _dp, _dp]
     _lib = lib
     return lib
 
@@ -181,3 +187,48 @@ def bwd_sample(q, k, v, dout, qrows, krows, causal: bool = False, scale: float |
     if rc:
         raise RuntimeError(f"fa_oracle_bwd_sample failed ({rc})")
     return dq, dk, dv
+
+
+def decode(q, k, v, causal: bool = False, scale: float | None = None, kv_lens=None):
+    """Decode-shaped forward: q [B,H,Nq,d] against k, v [B,H,Nk,d] whose first
+    kv_lens[b] rows are filled.  The Nq queries are the newest positions
+    (kv_len - Nq + t); with causal, query t sees keys j <= kv_len - Nq + t.
+    Returns (O [B,H,Nq,d], LSE [B,H,Nq]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B,H,Nq,d] and k, v [B,H,Nk,d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lens = None
+    if kv_lens is not None:
+        lens = np.ascontiguousarray(np.asarray(kv_lens), dtype=np.int32)
+        if lens.shape != (B,):
+            raise ValueError("kv_lens must have shape [B]")
+    o = np.empty((B, H, Nq, d), np.float64)
+    lse = np.empty((B, H, Nq), np.float64)
+    rc = _load().fa_oracle_decode(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(o, _dp),
+                                  _ptr(lse, _dp), B, H, Nq, Nk, d, int(bool(causal)),
+                                  float(scale), _ptr(lens, _i32p))
+    if rc:
+        raise RuntimeError(f"fa_oracle_decode failed ({rc})")
+    return o, lse
+
+
+def merge(o_parts, lse_parts):
+    """Fold S partial (O, LSE) results over disjoint key sets: o_parts [S, R, d],
+    lse_parts [S, R] (natural log, -inf = empty part).  Returns (O [R, d],
+    LSE [R]) in float64."""
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    if o_parts.ndim != 3 or lse_parts.shape != o_parts.shape[:2]:
+        raise ValueError("o_parts must be [S, R, d] and lse_parts [S, R]")
+    S, R, d = o_parts.shape
+    o = np.empty((R, d), np.float64)
+    lse = np.empty((R,), np.float64)
+    rc = _load().fa_oracle_merge(_ptr(o_parts, _dp), _ptr(lse_parts, _dp), S, R, d,
+                                 _ptr(o, _dp), _ptr(lse, _dp))
+    if rc:
+        raise RuntimeError(f"fa_oracle_merge failed ({rc})")
+    return o, lse

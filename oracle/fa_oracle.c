@@ -389,3 +389,129 @@ int fa_oracle_bwd_sample(const double *q, const double *k, const double *v,
     }
     return err;
 }
+
+/*
+ * Decode-shaped forward: Nq new query rows per (b, h) against a key/value
+ * cache of Nk rows, of which the first kv_len[b] are filled (all Nk when
+ * kv_lens is NULL).  The pages name this case -- the cache grows by one
+ * token per step and each step is a small matmul ("Attention" chapter of
+ * learn-kernels.com, paragraph on decoding) -- and the result is the same
+ * definition as above with a rectangular score matrix.
+ *
+ * Reading where the pages are silent: the Nq queries are the newest Nq
+ * positions of the sequence, so query t sits at position kv_len - Nq + t.
+ * Without the causal flag every query sees keys j < kv_len; with it, query t
+ * sees keys j <= kv_len - Nq + t (the square causal mask aligned at the
+ * bottom right; for Nq = 1 both are the same).  A query that sees no key has
+ * O = 0 and LSE = -inf.
+ *
+ * Layout: q and o are [B][H][Nq][d], k and v are [B][H][Nk][d], lse is
+ * [B][H][Nq].
+ */
+int fa_oracle_decode(const double *q, const double *k, const double *v,
+                     double *o, double *lse, int B, int H, int Nq, int Nk,
+                     int d, int causal, double scale, const int32_t *kv_lens)
+{
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
+        return 1;
+    const int64_t total = (int64_t)B * H * Nq;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)Nk);
+        if (!s) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < total; ++r) {
+                const int64_t bh = r / Nq;
+                const int t = (int)(r % Nq);
+                const int b = (int)(bh / H);
+                int len = kv_lens ? kv_lens[b] : Nk;
+                if (len > Nk)
+                    len = Nk;
+                /* keys j < visible are allowed for this query */
+                int visible = causal ? len - Nq + t + 1 : len;
+                if (visible < 0)
+                    visible = 0;
+                const double *qi = q + (size_t)r * d;
+                const double *kh = k + (size_t)bh * Nk * d;
+                const double *vh = v + (size_t)bh * Nk * d;
+                double *oi = o + (size_t)r * d;
+                for (int e = 0; e < d; ++e)
+                    oi[e] = 0.0;
+                if (visible == 0) {
+                    lse[r] = -INFINITY;
+                    continue;
+                }
+                /* move 1: scores; move 2: safe softmax; move 3: O = P V */
+                double m = -INFINITY;
+                for (int j = 0; j < visible; ++j) {
+                    s[j] = scale * dot(qi, kh + (size_t)j * d, d);
+                    if (s[j] > m)
+                        m = s[j];
+                }
+                double l = 0.0;
+                for (int j = 0; j < visible; ++j)
+                    l += exp(s[j] - m);
+                for (int j = 0; j < visible; ++j) {
+                    const double p = exp(s[j] - m) / l;
+                    for (int e = 0; e < d; ++e)
+                        oi[e] += p * vh[(size_t)j * d + e];
+                }
+                lse[r] = m + log(l);
+            }
+        }
+        free(s);
+    }
+    return err;
+}
+
+/*
+ * Combine S partial results of the same rows, each computed over a disjoint
+ * part of the keys: o_parts is [S][R][d] (each part's own normalised output)
+ * and lse_parts is [S][R] (each part's log-sum-exp, natural log, -inf for a
+ * part with no key).  The parts are folded in order with the two-block
+ * update of "FlashAttention: Mathematical Foundations, IO-Aware Tiling,
+ * Online Softmax, and Recomputation Dynamics", section "Incremental Online
+ * Updates", written in log-sum-exp form: with l = exp(LSE - m), the weight
+ * that page gives the first block's output, l1 exp(m1 - m_new) / l_new,
+ * equals exp(LSE1 - LSE_new), and likewise for the second block.
+ * The result is O [R][d] and LSE [R]; rows where every part is empty get
+ * O = 0 and LSE = -inf.
+ */
+int fa_oracle_merge(const double *o_parts, const double *lse_parts, int S,
+                    int64_t R, int d, double *o, double *lse)
+{
+    if (S <= 0 || R < 0 || d <= 0)
+        return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        double *oi = o + (size_t)r * d;
+        double L = -INFINITY;   /* running log-sum-exp of the folded parts */
+        for (int e = 0; e < d; ++e)
+            oi[e] = 0.0;
+        for (int s = 0; s < S; ++s) {
+            const double Ls = lse_parts[(size_t)s * R + r];
+            if (Ls == -INFINITY)
+                continue;   /* an empty part contributes nothing */
+            const double *os = o_parts + ((size_t)s * R + r) * d;
+            if (L == -INFINITY) {
+                for (int e = 0; e < d; ++e)
+                    oi[e] = os[e];
+                L = Ls;
+                continue;
+            }
+            /* m_new = max(m1, m2); l_new = l1 e^(m1-m_new) + l2 e^(m2-m_new) */
+            const double mx = L > Ls ? L : Ls;
+            const double Lnew = mx + log(exp(L - mx) + exp(Ls - mx));
+            const double w1 = exp(L - Lnew), w2 = exp(Ls - Lnew);
+            for (int e = 0; e < d; ++e)
+                oi[e] = w1 * oi[e] + w2 * os[e];
+            L = Lnew;
+        }
+        lse[r] = L;
+    }
+    return 0;
+}
