@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "bwd_dkdv": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
     "bwd_dq": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
     "bwd_sparse": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
+    "decode": "exact_io_aware_36_amd/csrc/fa_decode.hip",
 }
 
 
@@ -193,6 +194,110 @@ def cpu_baseline(inp, w, metric_flops, budget_s=15.0, seed=99):
     }
 
 
+def decode_accounting(B, H, nq, d, lens, causal=False):
+    """Flops and algorithmic bytes of one decode-shaped forward call: each
+    query row against the keys it sees (2 products, 2 d flops each per pair);
+    bytes = the visible K and V rows once + Q, O (bf16) + LSE (fp32)."""
+    pairs = 0
+    for L in lens:
+        for t in range(nq):
+            pairs += max(0, (L - nq + t + 1) if causal else L)
+    flops = 4.0 * d * H * pairs
+    kv_rows = H * sum(int(L) for L in lens)
+    nbytes = 2 * kv_rows * d * 2 + 2 * B * H * nq * d * 2 + B * H * nq * 4
+    return flops, nbytes
+
+
+def cpu_baseline_decode(inp, w, budget_s=15.0):
+    """Time the oracle's decode forward over the whole workload, repeated
+    until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    q = inp["q"].double().numpy()
+    k = inp["k"].double().numpy()
+    v = inp["v"].double().numpy()
+    lens = inp["kv_lens"].numpy() if inp["kv_lens"] is not None else None
+    reps, dt = 0, 0.0
+    while dt < budget_s:
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, causal=w.causal, scale=w.scale, kv_lens=lens)
+        dt += time.perf_counter() - t0
+        reps += 1
+    flops, _ = decode_accounting(inp["B"], inp["H"], w.nq, inp["d"],
+                                 lens if lens is not None else [inp["N"]] * inp["B"], w.causal)
+    return {"value": flops * reps / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"the whole workload, {reps} oracle fp64 decode call(s) in {dt:.1f} s",
+            "seconds": dt}
+
+
+def bench_decode(args, w, inp, fa, torch):
+    """One step = one fa_fwd_splitkv call (the split kernel and the merge)."""
+    B, H, N, d, nq = inp["B"], inp["H"], inp["N"], inp["d"], w.nq
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    lens_h = inp["kv_lens"] if inp["kv_lens"] is not None else torch.full((B,), N, dtype=torch.int32)
+    lens = lens_h.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
+    nbytes_ws = fa.fa_fwd_splitkv_workspace_bytes(B, H, nq, N, d, 0)
+    ws = torch.empty(max(nbytes_ws, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def launch():
+        fa.fa_fwd_splitkv(q, k, v, o, lse, ws, causal=w.causal, scale=w.scale, kv_lens=lens)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        launch()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)) / args.steps
+    flops, nbytes = decode_accounting(B, H, nq, d, lens_h.tolist(), w.causal)
+    gbs = nbytes / (call_ms * 1e-3) / 1e9
+    traffic = read_traffic("decode", w.name)
+    roofline = {"kernel": "decode", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "avg_launch_ms": round(call_ms, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_decode(inp, w, budget_s=args.cpu_budget)
+        cpu = {k2: (round(v2, 6) if isinstance(v2, float) else v2) for k2, v2 in cpu.items()}
+    line = {
+        "metric": "attention TFLOP/s fwd & fwd+bwd, % bf16 MFMA peak, N=256-16K, d=64/128",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "Nq": nq, "Nk": N, "d": d,
+                   "causal": w.causal, "pass": "fwd (decode, split keys)",
+                   "splits": fa.fa_splitkv_splits(B, H, N, 0), "flops_per_step": flops,
+                   "bytes_per_step": nbytes,
+                   "flop_convention": "4 d flops per (query row, visible key) pair"},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "detail": {"call_ms": round(call_ms, 4), "hbm_gbs": round(gbs, 1)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +330,8 @@ def main(argv=None):
         return 1
     w = workloads.WORKLOADS[args.workload]
     inp = workloads.make_inputs(w)
+    if w.nq is not None:
+        return bench_decode(args, w, inp, fa, torch)
     B, H, N, d = inp["B"], inp["H"], inp["N"], inp["d"]
     dev = torch.device("cuda:0")
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))

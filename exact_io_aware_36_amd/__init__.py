@@ -81,6 +81,15 @@ _lib.fa_bwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _i, _i, _vp, _sz, _vp]
 _lib.fa_fwd_blocksparse.restype = _i
 _lib.fa_fwd_blocksparse.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _i, _vp]
+_lib.fa_splitkv_splits.restype = _i
+_lib.fa_splitkv_splits.argtypes = [_i, _i, _i, _i]
+_lib.fa_fwd_splitkv_workspace_bytes.restype = _sz
+_lib.fa_fwd_splitkv_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.fa_fwd_splitkv.restype = _i
+_lib.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i,
+                                _vp, _sz, _vp]
+_lib.fa_merge.restype = _i
+_lib.fa_merge.argtypes = [_vp, _vp, _i, _i, _i, _vp, _vp, _i, _vp]
 
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP32 = 1
@@ -248,6 +257,47 @@ def fa_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, workspace, block_mask,
     _check_rc(rc, "fa_bwd_blocksparse")
 
 
+def fa_splitkv_splits(B: int, H: int, Nk: int, num_splits: int = 0) -> int:
+    return int(_lib.fa_splitkv_splits(B, H, Nk, num_splits))
+
+
+def fa_fwd_splitkv_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int,
+                                   num_splits: int = 0) -> int:
+    return int(_lib.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, workspace, causal=False, scale=None, kv_lens=None,
+                   num_splits=0, stream=None):
+    B, H, Nq, d = _shape(q)
+    Bk, Hk, Nk, dk = _shape(k)
+    _require((Bk, Hk, dk) == (B, H, d), "k must be [B, H, Nk, d] with q's B, H, d")
+    _same(k, v)
+    _same(q, o)
+    _require(k.dtype == q.dtype and k.device == q.device, "q and k must share dtype and device")
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * Nq,
+             "lse must be contiguous fp32 [B, H, Nq]")
+    if kv_lens is not None:
+        _require(kv_lens.dtype == torch.int32 and kv_lens.numel() == B, "kv_lens must be int32 [B]")
+    rc = _lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                             int(bool(causal)), _scale(scale, d), _ptr(kv_lens), int(num_splits),
+                             _dtype(q), _ptr(workspace), _ws_bytes(workspace), _stream(q, stream))
+    _check_rc(rc, "fa_fwd_splitkv")
+
+
+def fa_merge(o_parts, lse_parts, o, lse, stream=None):
+    _require(o_parts.dim() == 3 and o_parts.dtype == torch.float32 and o_parts.is_contiguous(),
+             "o_parts must be contiguous fp32 [S, R, d]")
+    S, R, d = (int(x) for x in o_parts.shape)
+    _require(lse_parts.dtype == torch.float32 and lse_parts.is_contiguous()
+             and tuple(lse_parts.shape) == (S, R), "lse_parts must be contiguous fp32 [S, R]")
+    _require(o.is_contiguous() and o.numel() == R * d, "o must be contiguous [R, d]")
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == R,
+             "lse must be contiguous fp32 [R]")
+    rc = _lib.fa_merge(_ptr(o_parts), _ptr(lse_parts), S, R, d, _ptr(o), _ptr(lse), _dtype(o),
+                       _stream(o_parts, stream))
+    _check_rc(rc, "fa_merge")
+
+
 # -- the same calls with torch-allocated outputs ------------------------------
 
 def fwd(q, k, v, causal=False, scale=None, kv_lens=None, tile_n=0, stream=None):
@@ -287,4 +337,28 @@ def fwd_blocksparse(q, k, v, block_mask, mask_block=128, scale=None, stream=None
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_block=mask_block, scale=scale,
                        stream=stream)
+    return o, lse
+
+
+def fwd_splitkv(q, k, v, causal=False, scale=None, kv_lens=None, num_splits=0, stream=None):
+    """Decode-shaped forward of q [B, H, Nq, d] against the cache k, v
+    [B, H, Nk, d]; return (O [B, H, Nq, d], LSE [B, H, Nq])."""
+    B, H, Nq, d = _shape(q)
+    Nk = int(k.shape[2]) if k.dim() == 4 else 0
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nbytes = fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    fa_fwd_splitkv(q, k, v, o, lse, ws, causal=causal, scale=scale, kv_lens=kv_lens,
+                   num_splits=num_splits, stream=stream)
+    return o, lse
+
+
+def merge(o_parts, lse_parts, out_dtype=torch.bfloat16, stream=None):
+    """Combine partial results o_parts [S, R, d], lse_parts [S, R]; return
+    (O [R, d] in out_dtype, LSE [R])."""
+    S, R, d = (int(x) for x in o_parts.shape)
+    o = torch.empty((R, d), dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty((R,), dtype=torch.float32, device=o_parts.device)
+    fa_merge(o_parts, lse_parts, o, lse, stream=stream)
     return o, lse

@@ -216,4 +216,102 @@ fa_status fa_bwd_blocksparse(const void *q, const void *k, const void *v, const 
     return from_hip(fa::launch_bwd_bf16(a, d, false, true, (hipStream_t)stream));
 }
 
+// Split plan of the split-KV forward: chunk keys per split (a multiple of
+// 32), S = ceil(Nk / chunk) splits.  The default aims at about 2048
+// workgroups (8 per CU) with at least 256 keys per split.
+static const int kMaxSplits = 1024;
+static void splitkv_plan(int B, int H, int Nk, int num_splits, int *S, int *chunk)
+{
+    int64_t s = num_splits;
+    if (s <= 0) {
+        const int64_t bh = (int64_t)B * H;
+        s = (2048 + bh - 1) / bh;
+        s = s < (Nk + 255) / 256 ? s : (Nk + 255) / 256;
+    }
+    s = s < (Nk + 31) / 32 ? s : (Nk + 31) / 32;
+    s = s < kMaxSplits ? s : kMaxSplits;
+    s = s < 1 ? 1 : s;
+    const int ch = (int)(((Nk + s - 1) / s + 31) / 32 * 32);
+    *chunk = ch;
+    *S = (Nk + ch - 1) / ch;
+}
+
+int fa_splitkv_splits(int B, int H, int Nk, int num_splits)
+{
+    if (B < 1 || H < 1 || Nk < 1 || num_splits < 0)
+        return 0;
+    int S, chunk;
+    splitkv_plan(B, H, Nk, num_splits, &S, &chunk);
+    return S;
+}
+
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits)
+{
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0 || (d != 64 && d != 128))
+        return 0;
+    int S, chunk;
+    splitkv_plan(B, H, Nk, num_splits, &S, &chunk);
+    if (S == 1)
+        return 0;
+    const size_t R = (size_t)B * H * Nq;
+    return round256((size_t)S * R * d * sizeof(float)) + round256((size_t)S * R * sizeof(float));
+}
+
+fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                         const int32_t *kv_lens, int num_splits, fa_dtype dtype,
+                         void *workspace, size_t workspace_bytes, fa_stream_t stream)
+{
+    if (!q || !k || !v || !o || !lse)
+        return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0)
+        return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale))
+        return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED;
+    const int64_t nmax = Nq > Nk ? Nq : Nk;
+    if ((int64_t)B * H * nmax * d >= ((int64_t)1 << 31))
+        return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4) || (kv_lens && !aligned(kv_lens, 4)))
+        return FA_ERR_INVALID_ARG;
+    if (Nq > 8 || dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    int S, chunk;
+    splitkv_plan(B, H, Nk, num_splits, &S, &chunk);
+    const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return FA_ERR_WORKSPACE;
+    const size_t R = (size_t)B * H * Nq;
+    float *o_part = (float *)workspace;
+    float *lse_part = S > 1 ? (float *)((char *)workspace + round256((size_t)S * R * d * sizeof(float)))
+                            : nullptr;
+    fa::DecodeArgs a{q, k, v, o, lse, o_part, lse_part, B, H, Nq, Nk, S, chunk, scale, kv_lens,
+                     causal != 0};
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = fa::launch_decode(a, d, s);
+    if (e != hipSuccess || S == 1)
+        return from_hip(e);
+    return from_hip(fa::launch_merge(o_part, lse_part, S, (int)R, d, o, lse, true, s));
+}
+
+fa_status fa_merge(const float *o_parts, const float *lse_parts, int S, int R, int d, void *o,
+                   float *lse, fa_dtype dtype, fa_stream_t stream)
+{
+    if (!o_parts || !lse_parts || !o || !lse)
+        return FA_ERR_INVALID_ARG;
+    if (S < 1 || R < 1 || d < 1 || d > 1024 || (int64_t)R * d >= ((int64_t)1 << 31))
+        return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32)
+        return FA_ERR_UNSUPPORTED;
+    if (!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(lse, 4) ||
+        !aligned(o, dtype == FA_DTYPE_BF16 ? 2 : 4))
+        return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_merge(o_parts, lse_parts, S, R, d, o, lse, dtype == FA_DTYPE_BF16,
+                                     (hipStream_t)stream));
+}
+
 } // extern "C"

@@ -41,6 +41,29 @@ enum class BwdStage { Dot, DkDv, Dq };
 hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, bool sparse, BwdStage stage,
                             hipStream_t s);
 
+// Decode-shaped forward with the keys split over workgroups.  q and o are
+// [B][H][Nq][D], k and v [B][H][Nk][D].  Split s covers keys
+// [s*chunk, (s+1)*chunk); with S == 1 the kernel writes o and lse directly,
+// otherwise each split writes its own normalised output and log-sum-exp to
+// o_part [S][B*H*Nq][D] and lse_part [S][B*H*Nq] for the merge kernel.
+struct DecodeArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    float *o_part, *lse_part;
+    int B, H, Nq, Nk, S, chunk;
+    float scale;
+    const int32_t *kv_lens;  // nullable device int32[B]
+    int causal;
+};
+hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t s);
+
+// Merge of S partial results per row: o_parts [S][R][d] fp32 (each part
+// normalised), lse_parts [S][R] (natural log, -inf = empty part) into o [R][d]
+// (bf16 when out_bf16, else fp32) and lse [R].
+hipError_t launch_merge(const float *o_parts, const float *lse_parts, int S, int R, int d,
+                        void *o, float *lse, bool out_bf16, hipStream_t s);
+
 constexpr int MAX_MASK_BLOCKS = 512;   // block-sparse: N <= 65536 with 128-blocks
 
 // Wave 0 of the workgroup lists, in increasing order, the indices i < n with

@@ -197,6 +197,64 @@ fa_status fa_bwd_blocksparse(const void *q, const void *k, const void *v, const 
                              const uint8_t *block_mask, int mask_block, fa_dtype dtype,
                              void *workspace, size_t workspace_bytes, fa_stream_t stream);
 
+/*
+ * Decode-shaped forward with the key range split over workgroups.  The pages
+ * single out decoding -- the key/value cache grows by one token per step and
+ * each step is a small, frequent product -- as the case that needs its own
+ * kernel ("Attention", learn-kernels.com, paragraph on decoding).  Each
+ * split computes its keys' normalised output and log-sum-exp, and the splits
+ * are combined by the two-block update of "FlashAttention: Mathematical
+ * Foundations, IO-Aware Tiling, Online Softmax, and Recomputation Dynamics",
+ * section "Incremental Online Updates" (the merge below).  The result is the
+ * same exact attention as fa_fwd, over a rectangular score matrix.
+ *   q, o     device bf16 [B][H][Nq][d]: the Nq newest query rows of each
+ *            sequence, 1 <= Nq <= 8
+ *   k, v     device bf16 [B][H][Nk][d]: the key/value cache
+ *   lse      device fp32 [B][H][Nq]
+ *   kv_lens  nullable device int32[B]: rows 0 .. kv_lens[b]-1 of batch entry
+ *            b's cache are filled (all Nk when NULL); values outside [0, Nk]
+ *            are clamped to it
+ *   causal   0: every query sees every filled key.  1: query t sits at
+ *            position kv_len - Nq + t and sees keys j <= kv_len - Nq + t
+ *            (for Nq = 1 both are the same)
+ *   num_splits  0 chooses the split count from B*H and Nk; otherwise the
+ *            requested count, lowered so that each split holds at least 32
+ *            keys (fa_splitkv_splits returns the count used)
+ *   workspace   device, 256-byte aligned, at least
+ *            fa_fwd_splitkv_workspace_bytes(...) bytes (may be NULL when that
+ *            is 0, i.e. when one split is used); overwritten
+ * A query that sees no key gets O = 0, LSE = -inf.
+ * Errors: FA_ERR_INVALID_ARG for null pointers, sizes < 1, num_splits < 0,
+ * a non-finite or non-positive scale, misalignment or B*H*max(Nq,Nk)*d >= 2^31;
+ * FA_ERR_UNSUPPORTED for d not in {64, 128}, Nq > 8 or dtype other than
+ * BF16; FA_ERR_WORKSPACE for a missing, small or misaligned workspace.
+ */
+int fa_splitkv_splits(int B, int H, int Nk, int num_splits);
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                         const int32_t *kv_lens, int num_splits, fa_dtype dtype,
+                         void *workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * Merge S partial results of the same R rows, each computed over a disjoint
+ * set of keys ("FlashAttention: Mathematical Foundations ...", section
+ * "Incremental Online Updates", in log-sum-exp form):
+ *     LSE = ln(sum_s exp(LSE_s)),   O = sum_s exp(LSE_s - LSE) * O_s.
+ * This is the combine step of fa_fwd_splitkv and of any split of one head's
+ * keys across calls or devices.
+ *   o_parts    device fp32 [S][R][d], each part's normalised output
+ *   lse_parts  device fp32 [S][R], natural log; -inf marks an empty part,
+ *              whose o_parts rows are ignored
+ *   o          device [R][d], dtype BF16 or FP32;  lse  device fp32 [R]
+ * Rows whose parts are all empty get O = 0 and LSE = -inf.
+ * Errors: FA_ERR_INVALID_ARG for null pointers, S < 1, R < 1, d < 1,
+ * d > 1024, R*d >= 2^31 or misaligned pointers (4 bytes; 2 for a bf16 o);
+ * FA_ERR_UNSUPPORTED for another dtype.
+ */
+fa_status fa_merge(const float *o_parts, const float *lse_parts, int S, int R, int d, void *o,
+                   float *lse, fa_dtype dtype, fa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -177,3 +177,59 @@ def bwd_sparse(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=1,
 ])
 def test_bwd_sparse_rejects(lib, kw, want):
     assert bwd_sparse(lib, **kw) == want
+
+
+def test_splitkv_plan(lib):
+    # default: about 2048 workgroups, at least 256 keys per split
+    assert lib.fa_splitkv_splits(8, 16, 16384, 0) == 16
+    assert lib.fa_splitkv_splits(1, 1, 100, 0) == 1
+    assert lib.fa_splitkv_splits(2, 2, 5000, 0) == 20
+    # requested counts are lowered so that each split has >= 32 keys
+    assert lib.fa_splitkv_splits(1, 1, 100, 5) == 4
+    assert lib.fa_splitkv_splits(1, 1, 300, 1000) == 10
+    assert lib.fa_splitkv_splits(1, 1, 1, 0) == 1
+    assert lib.fa_splitkv_splits(0, 1, 1, 0) == 0
+    assert lib.fa_splitkv_splits(1, 1, 100, -1) == 0
+    # workspace: fp32 partial O [S][R][d] and LSE [S][R], each rounded to 256 B
+    assert lib.fa_fwd_splitkv_workspace_bytes(8, 16, 1, 16384, 128, 0) == 16 * 128 * 128 * 4 + 16 * 128 * 4
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 3, 100, 64, 0) == 0        # one split
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 3, 100, 64, 4) == 4 * 3 * 64 * 4 + 256
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 100, 96, 0) == 0
+
+
+def splitkv(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=1, Nk=100000, d=128, causal=0,
+            scale=0.125, lens=None, ns=0, dtype=BF16, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, ns)
+    return lib.fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, lens, ns, dtype,
+                              ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(o=None), INVALID),
+    (dict(lse=None), INVALID), (dict(B=0), INVALID), (dict(Nq=0), INVALID), (dict(Nk=0), INVALID),
+    (dict(ns=-1), INVALID), (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(Nq=9), UNSUPPORTED),
+    (dict(dtype=FP32), UNSUPPORTED),
+    (dict(B=64, H=64, Nk=8192), INVALID),                    # B*H*Nk*d >= 2^31
+    (dict(q=MIS), INVALID), (dict(v=MIS), INVALID), (dict(lse=P + 2), INVALID),
+    (dict(lens=P + 1), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws=P + 64), WORKSPACE), (dict(ws_bytes=1024), WORKSPACE),
+])
+def test_splitkv_rejects(lib, kw, want):
+    assert splitkv(lib, **kw) == want
+
+
+def merge(lib, op=P, lp=P, S=4, R=10, d=128, o=P, lse=P, dtype=BF16):
+    return lib.fa_merge(op, lp, S, R, d, o, lse, dtype, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(op=None), INVALID), (dict(lp=None), INVALID), (dict(o=None), INVALID),
+    (dict(lse=None), INVALID), (dict(S=0), INVALID), (dict(R=0), INVALID), (dict(d=0), INVALID),
+    (dict(d=2048), INVALID), (dict(R=1 << 22, d=1024), INVALID), (dict(dtype=7), UNSUPPORTED),
+    (dict(op=P + 2), INVALID), (dict(lse=P + 1), INVALID), (dict(o=P + 1), INVALID),
+    (dict(o=P + 2, dtype=FP32), INVALID),
+])
+def test_merge_rejects(lib, kw, want):
+    assert merge(lib, **kw) == want

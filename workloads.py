@@ -5,7 +5,8 @@ Both the oracle side and the GPU side take their inputs from here.
 
 Recipe (every workload): one CPU ``torch.Generator`` seeded with the workload's
 seed draws, in this order, Q, K, V (and dO when the workload has a backward)
-as float32 ``randn`` of shape [B, H, N, d], each multiplied by the workload's
+as float32 ``randn`` of shape [B, H, N, d] (Q of a decode workload is
+[B, H, nq, d] against an N-row cache), each multiplied by the workload's
 input scale; then the key-padding lengths; then the block mask.  bf16
 workloads cast the float32 draws to bf16 with round-to-nearest-even (torch's
 ``.to(torch.bfloat16)``).  The pages measure on GPT-2, BERT-large, Long Range
@@ -34,6 +35,7 @@ class Workload:
     kv_len_range: tuple | None = None   # inclusive (lo, hi) for key padding
     sparse_frac: float | None = None    # nonzero block fraction for block-sparse
     mask_block: int = 128
+    nq: int | None = None                # decode: query rows per (b, h); N is then the cache length
     note: str = field(default="", compare=False)
 
     @property
@@ -60,6 +62,11 @@ WORKLOADS = {
     "block_sparse_fwdbwd": Workload("block_sparse_fwdbwd", 4, 16, 4096, 64, "bf16", False, 1005,
                                     sparse_frac=0.25, backward=True,
                                     note="block-sparse forward + backward, s=0.25"),
+    # one decode step: one new query row per (b, h) against a 16K-row cache
+    # filled to a per-sequence length (the decoding case of the pages)
+    "decode_splitkv": Workload("decode_splitkv", 8, 16, 16384, 128, "bf16", False, 1006,
+                               kv_len_range=(8192, 16384), nq=1,
+                               note="decode step, 1 query row vs a 16K cache, d=128"),
 }
 
 
@@ -97,10 +104,11 @@ def make_inputs(w: Workload, *, B: int | None = None, H: int | None = None,
     dt = torch_dtype(w)
     shape = (B, H, N, w.d)
 
-    def draw():
-        return (torch.randn(shape, generator=gen, dtype=torch.float32) * w.input_scale).to(dt)
+    def draw(shp=shape):
+        return (torch.randn(shp, generator=gen, dtype=torch.float32) * w.input_scale).to(dt)
 
-    out = {"q": draw(), "k": draw(), "v": draw()}
+    qshape = shape if w.nq is None else (B, H, w.nq, w.d)
+    out = {"q": draw(qshape), "k": draw(), "v": draw()}
     out["dout"] = torch.randn(shape, generator=gen, dtype=torch.float32).to(dt) if w.backward else None
     kv_lens = None
     if w.kv_len_range is not None:
@@ -114,7 +122,7 @@ def make_inputs(w: Workload, *, B: int | None = None, H: int | None = None,
         mask = block_mask(nb, w.sparse_frac, gen)
     out["block_mask"] = mask
     out.update(B=B, H=H, N=N, d=w.d, causal=w.causal, scale=w.scale, dtype=w.dtype,
-               mask_block=w.mask_block)
+               mask_block=w.mask_block, nq=w.nq)
     return out
 
 
