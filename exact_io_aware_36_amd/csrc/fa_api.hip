@@ -217,15 +217,17 @@ fa_status fa_bwd_blocksparse(const void *q, const void *k, const void *v, const 
 }
 
 // Split plan of the split-KV forward: chunk keys per split (a multiple of
-// 32), S = ceil(Nk / chunk) splits.  The default aims at about 2048
-// workgroups (8 per CU) with at least 256 keys per split.
+// 32), S = ceil(Nk / chunk) splits.  The default aims at 512 workgroups --
+// two per CU of the 256, which is what stays resident at the kernel's
+// register use, so the whole grid runs in one round -- with at least 256 keys
+// per split.
 static const int kMaxSplits = 1024;
 static void splitkv_plan(int B, int H, int Nk, int num_splits, int *S, int *chunk)
 {
     int64_t s = num_splits;
     if (s <= 0) {
         const int64_t bh = (int64_t)B * H;
-        s = (2048 + bh - 1) / bh;
+        s = (512 + bh - 1) / bh;
         s = s < (Nk + 255) / 256 ? s : (Nk + 255) / 256;
     }
     s = s < (Nk + 31) / 32 ? s : (Nk + 31) / 32;

@@ -180,8 +180,9 @@ def test_bwd_sparse_rejects(lib, kw, want):
 
 
 def test_splitkv_plan(lib):
-    # default: about 2048 workgroups, at least 256 keys per split
-    assert lib.fa_splitkv_splits(8, 16, 16384, 0) == 16
+    # default: about 512 workgroups, at least 256 keys per split
+    assert lib.fa_splitkv_splits(8, 16, 16384, 0) == 4
+    assert lib.fa_splitkv_splits(1, 16, 16384, 0) == 32
     assert lib.fa_splitkv_splits(1, 1, 100, 0) == 1
     assert lib.fa_splitkv_splits(2, 2, 5000, 0) == 20
     # requested counts are lowered so that each split has >= 32 keys
@@ -191,7 +192,7 @@ def test_splitkv_plan(lib):
     assert lib.fa_splitkv_splits(0, 1, 1, 0) == 0
     assert lib.fa_splitkv_splits(1, 1, 100, -1) == 0
     # workspace: fp32 partial O [S][R][d] and LSE [S][R], each rounded to 256 B
-    assert lib.fa_fwd_splitkv_workspace_bytes(8, 16, 1, 16384, 128, 0) == 16 * 128 * 128 * 4 + 16 * 128 * 4
+    assert lib.fa_fwd_splitkv_workspace_bytes(8, 16, 1, 16384, 128, 0) == 4 * 128 * 128 * 4 + 4 * 128 * 4
     assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 3, 100, 64, 0) == 0        # one split
     assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 3, 100, 64, 4) == 4 * 3 * 64 * 4 + 256
     assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 100, 96, 0) == 0
