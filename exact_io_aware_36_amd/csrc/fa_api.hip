@@ -11,8 +11,9 @@ namespace {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// d = 256 is built for the bf16 forward passes only (dense and block-sparse)
 fa_status check_common(const void *q, const void *k, const void *v, int B, int H, int N, int d,
-                       float scale)
+                       float scale, bool allow_256 = false)
 {
     if (!q || !k || !v)
         return FA_ERR_INVALID_ARG;
@@ -20,7 +21,7 @@ fa_status check_common(const void *q, const void *k, const void *v, int B, int H
         return FA_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !isfinite(scale))
         return FA_ERR_INVALID_ARG;
-    if (d != 64 && d != 128)
+    if (d != 64 && d != 128 && !(allow_256 && d == 256))
         return FA_ERR_UNSUPPORTED;
     if ((int64_t)B * H * N * d >= ((int64_t)1 << 31))
         return FA_ERR_INVALID_ARG;
@@ -51,7 +52,7 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
                     int H, int N, int d, int causal, float scale, const int32_t *kv_lens,
                     fa_dtype dtype, int tile_n, fa_stream_t stream)
 {
-    fa_status st = check_common(q, k, v, B, H, N, d, scale);
+    fa_status st = check_common(q, k, v, B, H, N, d, scale, dtype == FA_DTYPE_BF16);
     if (st != FA_OK)
         return st;
     if (!o || !lse || !aligned(o, 16) || !aligned(lse, 4))
@@ -61,7 +62,10 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale, kv_lens, nullptr, 0};
     hipStream_t s = (hipStream_t)stream;
     if (dtype == FA_DTYPE_BF16) {
-        if (tile_n != 0 && tile_n != 64 && tile_n != 128)
+        // key tiles: 64 or 128 at d = 64, 128; 32 or 64 at d = 256 (LDS)
+        const bool ok = d == 256 ? (tile_n == 0 || tile_n == 32 || tile_n == 64)
+                                 : (tile_n == 0 || tile_n == 64 || tile_n == 128);
+        if (!ok)
             return FA_ERR_UNSUPPORTED;
         return from_hip(fa::launch_fwd_bf16(a, d, tile_n, causal != 0, false, s));
     }
@@ -180,7 +184,7 @@ fa_status fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *
                              int B, int H, int N, int d, float scale, const uint8_t *block_mask,
                              int mask_block, fa_dtype dtype, fa_stream_t stream)
 {
-    fa_status st = check_common(q, k, v, B, H, N, d, scale);
+    fa_status st = check_common(q, k, v, B, H, N, d, scale, dtype == FA_DTYPE_BF16);
     if (st != FA_OK)
         return st;
     if (!o || !lse || !block_mask || !aligned(o, 16) || !aligned(lse, 4))

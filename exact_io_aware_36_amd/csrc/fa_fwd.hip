@@ -57,8 +57,12 @@ constexpr float TAU = 8.f;             // lazy-rescale threshold (log2 units)
 //
 // Tiles reach LDS by direct buffer->LDS loads into two stages; the loop is
 // unrolled by two so each half reads one stage while the other stage fills.
+//
+// D = 256 keeps the same schedule: Q's operands (64 registers) and the O^T
+// accumulator (128) need the 512-register budget of one wave per SIMD, and
+// two stages of 64-key K and V tiles take 128 KB of the 160 KB LDS.
 template <int D, int BC, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs p, float c_log2)
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs p, float c_log2)
 {
     constexpr int BR = 128;
     constexpr int KSTEPS = D / 16;         // k-steps of S^T over d
@@ -435,6 +439,10 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, int tile_n, bool causal, boo
         return launch_bf16_d_bc<128, 64>(a, causal, sparse, s);
     if (d == 128 && tile_n == 128)
         return launch_bf16_d_bc<128, 128>(a, causal, sparse, s);
+    if (d == 256 && tile_n == 64)
+        return launch_bf16_d_bc<256, 64>(a, causal, sparse, s);
+    if (d == 256 && tile_n == 32)
+        return launch_bf16_d_bc<256, 32>(a, causal, sparse, s);
     return hipErrorInvalidValue;
 }
 

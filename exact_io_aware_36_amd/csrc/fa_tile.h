@@ -1,7 +1,7 @@
 // fa_tile.h -- LDS tile layout and MFMA operand access shared by the
 // attention kernels (gfx950, wave64).
 //
-// A tile of R rows x D bf16 (D = 64 or 128) sits in LDS row-major with no
+// A tile of R rows x D bf16 (D = 64, 128 or 256) sits in LDS row-major with no
 // padding, its 16-byte chunks permuted within each row by an XOR swizzle.
 // Two access patterns read it:
 //   * ld_row8: lane l reads 8 consecutive columns of row r (one 16-byte
@@ -14,8 +14,10 @@
 //     reads 4 tile rows x 64 bytes per half-wave and transposes in hardware.
 // The swizzle makes both patterns free of bank conflicts (64 banks x 4 B):
 // for D = 128 every row is one 256-byte bank window and the chunk index is
-// XORed with ((r & 3) << 2 | (r >> 2) & 3); for D = 64 two rows share a
-// window and the chunk index is XORed with ((r >> 1) & 1) << 2 | (r >> 2) & 3.
+// XORed with ((r & 3) << 2 | (r >> 2) & 3); for D = 256 a row is two whole
+// windows and the same XOR is applied to the low four bits of the chunk
+// index; for D = 64 two rows share a window and the chunk index is XORed
+// with ((r >> 1) & 1) << 2 | (r >> 2) & 3.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,8 +56,8 @@ __device__ __forceinline__ float pair_sum(float x)
 template <int D>
 __device__ __forceinline__ int swz(int row)
 {
-    static_assert(D == 64 || D == 128, "head dim");
-    if constexpr (D == 128)
+    static_assert(D == 64 || D == 128 || D == 256, "head dim");
+    if constexpr (D >= 128)   // D = 256: two bank windows per row, same low-bit XOR
         return ((row & 3) << 2) | ((row >> 2) & 3);
     else
         return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);

@@ -39,8 +39,11 @@
  *    contents of device buffers (kv_lens values, mask bytes) are not checked:
  *    kv_lens values outside [0, N] are undefined behaviour.
  *  - Supported: d in {64, 128}; dtype BF16 everywhere; dtype FP32 for the
- *    dense forward only.  bf16 tensors are IEEE bfloat16, rounded to nearest
- *    even on store; all accumulation is fp32.
+ *    dense forward only.  d = 256 for the bf16 forward passes (fa_fwd,
+ *    fa_fwd_ex, fa_fwd_blocksparse): the large head dimension at which the
+ *    tiling loosens ("The Attention Matrix You Never Write Down", section
+ *    "What it buys, and where the analysis bites").  bf16 tensors are IEEE
+ *    bfloat16, rounded to nearest even on store; all accumulation is fp32.
  *  - Sizes: B, H, N >= 1 and B*H*N*d < 2^31.
  *  - Alignment: tensor pointers 16-byte aligned, LSE and kv_lens 4-byte
  *    aligned, the backward workspace 256-byte aligned (FA_ERR_INVALID_ARG,
@@ -84,7 +87,7 @@ const char *fa_status_str(fa_status s);
  *   kv_lens   nullable device int32[B] key-padding lengths
  * Errors: FA_ERR_INVALID_ARG for a null q/k/v/o/lse, B/H/N < 1, a
  * non-finite or non-positive scale, or B*H*N*d >= 2^31; FA_ERR_UNSUPPORTED
- * for d not in {64, 128} or an unknown dtype.
+ * for d not in {64, 128} (bf16: {64, 128, 256}) or an unknown dtype.
  */
 fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                  int B, int H, int N, int d, int causal, float scale,
@@ -95,7 +98,9 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  * pages' block-size constraint B_r*d + 2*B_c*d <= M, "FlashAttention:
  * Mathematical Foundations ...", section "IO-Aware Tiling Algorithm").
  * tile_n = 0 picks the default (64 for bf16, 32 for fp32); 64 and 128 are
- * built for bf16 and 32 for fp32.  Other values give FA_ERR_UNSUPPORTED.
+ * built for bf16 at d = 64 and 128, 32 and 64 for bf16 at d = 256 (two
+ * stages of 128-key tiles would not fit in LDS), and 32 for fp32.  Other
+ * values give FA_ERR_UNSUPPORTED.
  * Results equal fa_fwd's up to rounding order.
  */
 fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,

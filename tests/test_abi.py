@@ -81,8 +81,8 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, scale=0
     (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(scale=float("nan")), INVALID),
-    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=0), UNSUPPORTED),
-    (dict(dtype=7), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED), (dict(d=256, dtype=FP32), UNSUPPORTED), (dict(d=0), UNSUPPORTED),
+    (dict(d=512), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
     (dict(B=1 << 14, H=16, N=1 << 14, d=64), INVALID),      # B*H*N*d >= 2^31
     (dict(q=MIS), INVALID), (dict(o=MIS), INVALID), (dict(lse=P + 2), INVALID),
     (dict(lens=P + 1), INVALID),
@@ -95,6 +95,7 @@ def test_fwd_rejects(lib, kw, want):
     (dict(tile=32), UNSUPPORTED), (dict(tile=256), UNSUPPORTED), (dict(tile=-1), UNSUPPORTED),
     (dict(tile=64, dtype=FP32), UNSUPPORTED), (dict(tile=16, dtype=FP32), UNSUPPORTED),
     (dict(tile=64, d=80), UNSUPPORTED), (dict(tile=64, q=None), INVALID),
+    (dict(tile=128, d=256), UNSUPPORTED), (dict(tile=32, d=128), UNSUPPORTED),
 ])
 def test_fwd_ex_rejects(lib, kw, want):
     assert fwd(lib, **kw) == want
@@ -112,7 +113,7 @@ def bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=2, N=256,
     (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(do=None), INVALID),
     (dict(lse=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
     (dict(dv=None), INVALID), (dict(N=0), INVALID), (dict(scale=0.0), INVALID),
-    (dict(d=32), UNSUPPORTED), (dict(dtype=FP32), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dtype=FP32), UNSUPPORTED),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
     (dict(ws=P + 16), WORKSPACE), (dict(dq=MIS), INVALID),
 ])

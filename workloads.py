@@ -62,6 +62,9 @@ WORKLOADS = {
     "block_sparse_fwdbwd": Workload("block_sparse_fwdbwd", 4, 16, 4096, 64, "bf16", False, 1005,
                                     sparse_frac=0.25, backward=True,
                                     note="block-sparse forward + backward, s=0.25"),
+    # the large head dimension at which the pages say the tiling loosens
+    "d256_causal": Workload("d256_causal", 2, 16, 8192, 256, "bf16", True, 1007, input_scale=0.5,
+                            note="causal forward at head dim 256"),
     # one decode step: one new query row per (b, h) against a 16K-row cache
     # filled to a per-sequence length (the decoding case of the pages)
     "decode_splitkv": Workload("decode_splitkv", 8, 16, 16384, 128, "bf16", False, 1006,
