@@ -38,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 
 # kernel name (as rocprofv3 reports it) -> source file, for the traffic
@@ -49,6 +50,7 @@ KERNEL_SOURCES = {
     "bwd_dq": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
     "bwd_sparse": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
     "decode": "exact_io_aware_36_amd/csrc/fa_decode.hip",
+    "fwd_fp8": "exact_io_aware_36_amd/csrc/fa_fp8.hip",
 }
 
 
@@ -298,6 +300,85 @@ def bench_decode(args, w, inp, fa, torch):
     return 0
 
 
+def bench_fp8(args, w, inp, fa, torch):
+    """One step = one fa_fwd_fp8 call on inputs already quantised in HBM
+    (Q, K rotated with random signs; the quantiser is timed on the side)."""
+    import workloads
+
+    B, H, N, d = inp["B"], inp["H"], inp["N"], inp["d"]
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    signs = workloads.random_signs(d, w.seed).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def quantize():
+        q8, qs = fa.quantize_fp8(q, 128, signs)
+        k8, ks = fa.quantize_fp8(k, 128, signs)
+        v8t, vs = fa.quantize_fp8(v, 0, None, transpose=True)
+        return q8, qs, k8, ks, v8t, vs
+
+    q8, qs, k8, ks, v8t, vs = quantize()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def launch():
+        fa.fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, o, lse, causal=w.causal, scale=w.scale)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        launch()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)) / args.steps
+    flops = fwd_flops(B, H, N, d, w.causal)
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    # the quantiser, for context (not part of the step)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        quantize()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    roofline = {"kernel": "fwd_fp8", "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+                "traffic": read_traffic("fwd_fp8", w.name), "avg_launch_ms": round(call_ms, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, w, flops, budget_s=args.cpu_budget)
+        cpu = {k2: (round(v2, 6) if isinstance(v2, float) else v2) for k2, v2 in cpu.items()}
+    line = {
+        "metric": "attention TFLOP/s fwd & fwd+bwd, % bf16 MFMA peak, N=256-16K, d=64/128",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "pass": "fwd (FP8 E4M3 operands, fp32 accumulation)", "flops_per_step": flops,
+                   "pct_fp8_mfma_peak": round(100 * achieved / MFMA_FP8_PEAK_TFLOPS, 2),
+                   "flop_convention": "fwd 4N^2dBH (x1/2 causal)"},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "detail": {"call_ms": round(call_ms, 4), "quantize_qkv_ms": round(e0.elapsed_time(e1) / 5, 4)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +413,8 @@ def main(argv=None):
     inp = workloads.make_inputs(w)
     if w.nq is not None:
         return bench_decode(args, w, inp, fa, torch)
+    if w.fp8:
+        return bench_fp8(args, w, inp, fa, torch)
     B, H, N, d = inp["B"], inp["H"], inp["N"], inp["d"]
     dev = torch.device("cuda:0")
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))

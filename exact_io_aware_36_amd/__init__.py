@@ -88,6 +88,12 @@ _lib.fa_fwd_splitkv_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.fa_fwd_splitkv.restype = _i
 _lib.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i,
                                 _vp, _sz, _vp]
+_lib.fa_quantize_fp8_workspace_bytes.restype = _sz
+_lib.fa_quantize_fp8_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+_lib.fa_quantize_fp8.restype = _i
+_lib.fa_quantize_fp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _sz, _vp]
+_lib.fa_fwd_fp8.restype = _i
+_lib.fa_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp]
 _lib.fa_merge.restype = _i
 _lib.fa_merge.argtypes = [_vp, _vp, _i, _i, _i, _vp, _vp, _i, _vp]
 
@@ -298,6 +304,41 @@ def fa_merge(o_parts, lse_parts, o, lse, stream=None):
     _check_rc(rc, "fa_merge")
 
 
+def fa_quantize_fp8_workspace_bytes(B: int, H: int, N: int, d: int, block_rows: int = 128) -> int:
+    return int(_lib.fa_quantize_fp8_workspace_bytes(B, H, N, d, block_rows))
+
+
+def fa_quantize_fp8(x, x8, descale, block_rows=128, signs=None, transpose=False, workspace=None,
+                    stream=None):
+    B, H, N, d = _shape(x)
+    _require(x.dtype == torch.bfloat16 and x.is_contiguous(), "x must be contiguous bf16")
+    _require(x8.dtype == torch.uint8 and x8.is_contiguous() and x8.numel() == x.numel(),
+             "x8 must be contiguous uint8 with x's element count")
+    nblk = (N + 127) // 128 if block_rows else 1
+    _require(descale.dtype == torch.float32 and descale.is_contiguous()
+             and descale.numel() == B * H * nblk, "descale has the wrong size")
+    if signs is not None:
+        _require(signs.dtype == torch.float32 and signs.numel() == d, "signs must be fp32 [d]")
+    rc = _lib.fa_quantize_fp8(_ptr(x), _ptr(x8), _ptr(descale), B, H, N, d, int(block_rows),
+                              _ptr(signs), int(bool(transpose)), _ptr(workspace),
+                              _ws_bytes(workspace), _stream(x, stream))
+    _check_rc(rc, "fa_quantize_fp8")
+
+
+def fa_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, o, lse, causal=False, scale=None,
+               kv_lens=None, stream=None):
+    B, H, N, d = _shape(o)
+    for t in (q8, k8, v8t):
+        _require(t.dtype == torch.uint8 and t.is_contiguous() and t.numel() == B * H * N * d,
+                 "q8, k8, v8t must be contiguous uint8 with o's element count")
+    _require(o.dtype == torch.bfloat16 and o.is_contiguous(), "o must be contiguous bf16")
+    _require(lse.dtype == torch.float32 and lse.numel() == B * H * N, "lse must be fp32 [B, H, N]")
+    rc = _lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_descale), _ptr(k_descale),
+                         _ptr(v_descale), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                         _scale(scale, d), _ptr(kv_lens), _stream(o, stream))
+    _check_rc(rc, "fa_fwd_fp8")
+
+
 # -- the same calls with torch-allocated outputs ------------------------------
 
 def fwd(q, k, v, causal=False, scale=None, kv_lens=None, tile_n=0, stream=None):
@@ -361,4 +402,29 @@ def merge(o_parts, lse_parts, out_dtype=torch.bfloat16, stream=None):
     o = torch.empty((R, d), dtype=out_dtype, device=o_parts.device)
     lse = torch.empty((R,), dtype=torch.float32, device=o_parts.device)
     fa_merge(o_parts, lse_parts, o, lse, stream=stream)
+    return o, lse
+
+
+def quantize_fp8(x, block_rows=128, signs=None, transpose=False, stream=None):
+    """Return (codes uint8, descale fp32) of bf16 x [B, H, N, d]."""
+    B, H, N, d = _shape(x)
+    shape = (B, H, d, N) if transpose else (B, H, N, d)
+    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    nblk = (N + 127) // 128 if block_rows else 1
+    descale = torch.empty((B, H, nblk) if block_rows else (B, H), dtype=torch.float32, device=x.device)
+    nbytes = fa_quantize_fp8_workspace_bytes(B, H, N, d, block_rows)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    fa_quantize_fp8(x, x8, descale, block_rows=block_rows, signs=signs, transpose=transpose,
+                    workspace=ws, stream=stream)
+    return x8, descale
+
+
+def fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, causal=False, scale=None, kv_lens=None,
+            stream=None):
+    """FP8 forward on quantised inputs; return (O bf16 [B, H, N, d], LSE)."""
+    B, H, N, d = (int(x) for x in q8.shape)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, o, lse, causal=causal, scale=scale,
+               kv_lens=kv_lens, stream=stream)
     return o, lse

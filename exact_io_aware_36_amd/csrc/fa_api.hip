@@ -320,4 +320,55 @@ fa_status fa_merge(const float *o_parts, const float *lse_parts, int S, int R, i
                                      (hipStream_t)stream));
 }
 
+size_t fa_quantize_fp8_workspace_bytes(int B, int H, int N, int d, int block_rows)
+{
+    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || block_rows != 0)
+        return 0;
+    return round256((size_t)B * H * ((N + 127) / 128) * sizeof(float));
+}
+
+fa_status fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H, int N, int d,
+                          int block_rows, const float *signs, int transpose, void *workspace,
+                          size_t workspace_bytes, fa_stream_t stream)
+{
+    if (!x || !x8 || !descale)
+        return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || (block_rows != 0 && block_rows != 128))
+        return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * N * d >= ((int64_t)1 << 31) || (transpose && N % 16 != 0))
+        return FA_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(descale, 4) || (signs && !aligned(signs, 4)))
+        return FA_ERR_INVALID_ARG;
+    const size_t need = fa_quantize_fp8_workspace_bytes(B, H, N, d, block_rows);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return FA_ERR_WORKSPACE;
+    return from_hip(fa::launch_quant_fp8(x, x8, descale, (float *)workspace, signs, B, H, N, d,
+                                         block_rows == 0, transpose != 0, (hipStream_t)stream));
+}
+
+fa_status fa_fwd_fp8(const void *q8, const void *k8, const void *v8t, const float *q_descale,
+                     const float *k_descale, const float *v_descale, void *o, float *lse, int B,
+                     int H, int N, int d, int causal, float scale, const int32_t *kv_lens,
+                     fa_stream_t stream)
+{
+    if (!q8 || !k8 || !v8t || !q_descale || !k_descale || !v_descale || !o || !lse)
+        return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || N % 16 != 0)
+        return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale))
+        return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * N * d >= ((int64_t)1 << 31))
+        return FA_ERR_INVALID_ARG;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8t, 16) || !aligned(o, 16) ||
+        !aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(v_descale, 4) ||
+        !aligned(lse, 4) || (kv_lens && !aligned(kv_lens, 4)))
+        return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, o, lse, B, H,
+                                       N, d, causal != 0, scale, kv_lens, (hipStream_t)stream));
+}
+
 } // extern "C"

@@ -64,6 +64,20 @@ hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t s);
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int S, int R, int d,
                         void *o, float *lse, bool out_bf16, hipStream_t s);
 
+// FP8 (E4M3) quantiser: per 128-row block (per_head = false) or one scale per
+// (b, h) (per_head = true, amax_ws [B][H][ceil(N/128)] scratch); signs
+// (nullable) applies the random-sign Hadamard rotation; transpose writes
+// [B][H][d][N].
+hipError_t launch_quant_fp8(const void *x, void *x8, float *descale, float *amax_ws,
+                            const float *signs, int B, int H, int N, int d, bool per_head,
+                            bool transpose, hipStream_t s);
+// FP8 forward: q8, k8 [B][H][N][d] E4M3, v8t [B][H][d][N] E4M3; qs, ks
+// [B][H][ceil(N/128)] descales, vs [B][H]; o bf16, lse fp32.
+hipError_t launch_fwd_fp8(const void *q8, const void *k8, const void *v8t, const float *qs,
+                          const float *ks, const float *vs, void *o, float *lse, int B, int H,
+                          int N, int d, bool causal, float scale, const int32_t *kv_lens,
+                          hipStream_t s);
+
 constexpr int MAX_MASK_BLOCKS = 512;   // block-sparse: N <= 65536 with 128-blocks
 
 // Wave 0 of the workgroup lists, in increasing order, the indices i < n with

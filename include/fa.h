@@ -260,6 +260,53 @@ fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, f
 fa_status fa_merge(const float *o_parts, const float *lse_parts, int S, int R, int d, void *o,
                    float *lse, fa_dtype dtype, fa_stream_t stream);
 
+/*
+ * Block-quantised FP8 forward.  The pages describe it as FP8 matrix products
+ * on block-quantised operands with dynamic scaling ("FlashAttention:
+ * Mathematical Foundations ...", section "FlashAttention-3", item on
+ * low-precision FP8 support), made more accurate by incoherent processing
+ * ("Attention", learn-kernels.com, paragraph on Hopper).  Format: OCP E4M3
+ * ("FN": bias 7, largest finite 448, no infinities), one byte per element.
+ * Each block's largest magnitude maps to 448: code = E4M3(x * (448 / amax)),
+ * descale = amax / 448 (fp32; an all-zero block gets descale 1).
+ *
+ * fa_quantize_fp8: bf16 x [B][H][N][d] -> E4M3 codes x8 and descales.
+ *   block_rows  128: one scale per 128 consecutive rows of a (b, h), descale
+ *               [B][H][ceil(N/128)] (the layout fa_fwd_fp8 takes for Q, K);
+ *               0: one scale per (b, h), descale [B][H] (V)
+ *   signs       nullable device fp32[d] of +1/-1: before quantising, multiply
+ *               every row by R = diag(signs) H_d / sqrt(d) (H_d the Sylvester
+ *               Hadamard matrix; fast Walsh-Hadamard butterflies in fp32).
+ *               Pass the same signs for Q and K and none for V: R is
+ *               orthogonal, so the scores are unchanged
+ *   transpose   0: x8 [B][H][N][d]; 1: x8 [B][H][d][N] (the layout fa_fwd_fp8
+ *               takes for V); needs N % 16 == 0
+ *   workspace   block_rows = 0 only: fa_quantize_fp8_workspace_bytes(...)
+ *               bytes, 256-byte aligned (may be NULL when that is 0)
+ * Errors: FA_ERR_INVALID_ARG for null pointers, sizes < 1, block_rows not
+ * in {0, 128}, B*H*N*d >= 2^31, transpose with N % 16 != 0, misalignment
+ * (x, x8: 16 bytes; descale, signs: 4); FA_ERR_UNSUPPORTED for d not in
+ * {64, 128}; FA_ERR_WORKSPACE for a missing, small or misaligned workspace.
+ *
+ * fa_fwd_fp8: O (bf16) and LSE of exact attention on the dequantised
+ * inputs, with the probabilities rounded to E4M3 on chip for the P V product
+ * (their row sum is taken before rounding).  q8, k8: [B][H][N][d] codes with
+ * q_descale, k_descale [B][H][ceil(N/128)]; v8t: [B][H][d][N] codes with
+ * v_descale [B][H]; other arguments as fa_fwd.  N must be a multiple of 16.
+ * Codes must not be NaN.
+ * Errors: FA_ERR_INVALID_ARG for null pointers, sizes < 1, N % 16 != 0, a
+ * non-finite or non-positive scale, B*H*N*d >= 2^31, misalignment;
+ * FA_ERR_UNSUPPORTED for d not in {64, 128}.
+ */
+size_t fa_quantize_fp8_workspace_bytes(int B, int H, int N, int d, int block_rows);
+fa_status fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H, int N, int d,
+                          int block_rows, const float *signs, int transpose, void *workspace,
+                          size_t workspace_bytes, fa_stream_t stream);
+fa_status fa_fwd_fp8(const void *q8, const void *k8, const void *v8t, const float *q_descale,
+                     const float *k_descale, const float *v_descale, void *o, float *lse, int B,
+                     int H, int N, int d, int causal, float scale, const int32_t *kv_lens,
+                     fa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -160,9 +160,12 @@ def reference(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, scale=N
     return O, L, (Q, K, V)
 
 
-def p_quant_bound(Q, K, V, lse, causal=False, scale=None, kv_lens=None, n_slack=None) -> np.ndarray:
-    """Element-wise bound on |O_kernel - O_reference| caused by rounding the
-    probabilities to E4M3 before the P V product (float64 [B, H, N, d]).
+def p_quant_bound_rows(q_rows, i_rows, K, V, lse_rows, causal=False, scale=None, kv_len=None,
+                       n_slack=None) -> np.ndarray:
+    """Element-wise bound on |O_kernel - O_reference| for some query rows of
+    one head (q_rows [n, d] at positions i_rows, K and V [N, d], lse_rows
+    their reference LSE), caused by rounding the probabilities to E4M3 before
+    the P V product.
 
     The kernel forms p~_ij = 2^(s_ij log2 e - m) with a reference m no larger
     than the row's true maximum, so p~_ij >= P_ij l*_i with
@@ -173,26 +176,35 @@ def p_quant_bound(Q, K, V, lse, causal=False, scale=None, kv_lens=None, n_slack=
         sum_j |v_j| max(2^-4 P_ij, [P_ij l*_i < 2^-6] 2^-10 / l*_i).
     A relative slack of (1e-4 + n 2^-24) on sum_j P_ij |v_j| covers the fp32
     exponentials and sums (n = number of keys)."""
-    B, H, N, d = Q.shape
+    N, d = K.shape
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    bound = np.empty((B, H, N, d))
+    kvl = N if kv_len is None else int(kv_len)
     j = np.arange(N)
+    i = np.asarray(i_rows)
+    s = scale * (np.asarray(q_rows, np.float64) @ K.T)
+    allowed = (j[None, :] < kvl) & ((j[None, :] <= i[:, None]) | (not causal))
+    s = np.where(allowed, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    fin = np.isfinite(mx)
+    mx = np.where(fin, mx, 0.0)
+    lstar = np.exp(s - mx).sum(axis=1, keepdims=True)
+    lse = np.asarray(lse_rows, np.float64)
+    P = np.where(fin & allowed, np.exp(s - np.where(np.isfinite(lse), lse, 0.0)[:, None]), 0.0)
+    small = (P * lstar) < 2.0 ** -6
+    w = np.maximum(2.0 ** -4 * P, np.where(small & allowed, 2.0 ** -10 / np.maximum(lstar, 1.0), 0.0))
+    n = N if n_slack is None else n_slack
+    return w @ np.abs(V) + (1e-4 + n * 2.0 ** -24) * (P @ np.abs(V))
+
+
+def p_quant_bound(Q, K, V, lse, causal=False, scale=None, kv_lens=None, n_slack=None) -> np.ndarray:
+    """p_quant_bound_rows for every row of [B, H, N, d] operands."""
+    B, H, N, d = Q.shape
+    bound = np.empty((B, H, N, d))
+    rows = np.arange(N)
     for b in range(B):
-        kvl = N if kv_lens is None else int(kv_lens[b])
+        kvl = None if kv_lens is None else int(kv_lens[b])
         for h in range(H):
-            s = scale * (Q[b, h] @ K[b, h].T)
-            allowed = (j[None, :] < kvl) & ((j[None, :] <= j[:, None]) | (not causal))
-            s = np.where(allowed, s, -np.inf)
-            mx = s.max(axis=1, keepdims=True)
-            fin = np.isfinite(mx)
-            mx = np.where(fin, mx, 0.0)
-            e = np.exp(s - mx)
-            lstar = e.sum(axis=1, keepdims=True)
-            P = np.where(fin, np.exp(s - np.where(np.isfinite(lse[b, h]), lse[b, h], 0.0)[:, None]), 0.0)
-            P = np.where(allowed, P, 0.0)
-            small = (P * lstar) < 2.0 ** -6
-            w = np.maximum(2.0 ** -4 * P, np.where(small & allowed, 2.0 ** -10 / np.maximum(lstar, 1.0), 0.0))
-            n = N if n_slack is None else n_slack
-            bound[b, h] = w @ np.abs(V[b, h]) + (1e-4 + n * 2.0 ** -24) * (P @ np.abs(V[b, h]))
+            bound[b, h] = p_quant_bound_rows(Q[b, h], rows, K[b, h], V[b, h], lse[b, h], causal,
+                                             scale, kvl, n_slack)
     return bound

@@ -235,3 +235,40 @@ def merge(lib, op=P, lp=P, S=4, R=10, d=128, o=P, lse=P, dtype=BF16):
 ])
 def test_merge_rejects(lib, kw, want):
     assert merge(lib, **kw) == want
+
+
+def quant(lib, x=P, x8=P, ds=P, B=1, H=1, N=256, d=128, br=128, signs=None, tr=0, ws=None,
+          ws_bytes=0):
+    return lib.fa_quantize_fp8(x, x8, ds, B, H, N, d, br, signs, tr, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), INVALID), (dict(x8=None), INVALID), (dict(ds=None), INVALID),
+    (dict(N=0), INVALID), (dict(br=64), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(d=256), UNSUPPORTED), (dict(tr=1, N=200), INVALID), (dict(x=MIS), INVALID),
+    (dict(ds=P + 2), INVALID), (dict(signs=P + 2), INVALID),
+    (dict(br=0), WORKSPACE), (dict(br=0, ws=P, ws_bytes=16), WORKSPACE),
+])
+def test_quantize_fp8_rejects(lib, kw, want):
+    assert quant(lib, **kw) == want
+
+
+def test_quantize_fp8_workspace(lib):
+    assert lib.fa_quantize_fp8_workspace_bytes(2, 3, 300, 128, 0) == 256      # 18 floats -> 256 B
+    assert lib.fa_quantize_fp8_workspace_bytes(1, 16, 16384, 128, 0) == 16 * 128 * 4
+    assert lib.fa_quantize_fp8_workspace_bytes(1, 16, 16384, 128, 128) == 0
+
+
+def fwd8(lib, q=P, k=P, v=P, qs=P, ks=P, vs=P, o=P, lse=P, B=1, H=1, N=256, d=128, causal=0,
+         scale=0.125, lens=None):
+    return lib.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, H, N, d, causal, scale, lens, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(vs=None), INVALID), (dict(lse=None), INVALID),
+    (dict(N=200), INVALID), (dict(N=0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(d=256), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(v=MIS), INVALID),
+    (dict(ks=P + 1), INVALID), (dict(lens=P + 2), INVALID), (dict(B=1 << 12, H=64, N=4096), INVALID),
+])
+def test_fwd_fp8_rejects(lib, kw, want):
+    assert fwd8(lib, **kw) == want

@@ -36,6 +36,7 @@ class Workload:
     sparse_frac: float | None = None    # nonzero block fraction for block-sparse
     mask_block: int = 128
     nq: int | None = None                # decode: query rows per (b, h); N is then the cache length
+    fp8: bool = False                    # run through the block-quantised FP8 forward
     note: str = field(default="", compare=False)
 
     @property
@@ -65,6 +66,11 @@ WORKLOADS = {
     # the large head dimension at which the pages say the tiling loosens
     "d256_causal": Workload("d256_causal", 2, 16, 8192, 256, "bf16", True, 1007, input_scale=0.5,
                             note="causal forward at head dim 256"),
+    # the long-context causal shape through the block-quantised FP8 forward
+    # (Q, K rotated with random signs drawn after the mask, seed 1008)
+    "long_context_fp8": Workload("long_context_fp8", 1, 16, 16384, 128, "bf16", True, 1008,
+                                 input_scale=0.5, fp8=True,
+                                 note="long-context causal forward, FP8 E4M3"),
     # one decode step: one new query row per (b, h) against a 16K-row cache
     # filled to a per-sequence length (the decoding case of the pages)
     "decode_splitkv": Workload("decode_splitkv", 8, 16, 16384, 128, "bf16", False, 1006,
@@ -146,6 +152,13 @@ def random_qkv(B: int, H: int, N: int, d: int, seed: int, dtype=torch.bfloat16,
 def random_lengths(B: int, lo: int, hi: int, seed: int) -> torch.Tensor:
     gen = torch.Generator().manual_seed(seed)
     return torch.randint(lo, hi + 1, (B,), generator=gen, dtype=torch.int32)
+
+
+def random_signs(d: int, seed: int) -> torch.Tensor:
+    """float32 [d] of +1/-1, each sign an independent fair draw (the random
+    signs of the FP8 path's incoherent processing)."""
+    gen = torch.Generator().manual_seed(seed)
+    return (torch.randint(0, 2, (d,), generator=gen, dtype=torch.int32) * 2 - 1).to(torch.float32)
 
 
 def random_block_mask(nb: int, frac: float, seed: int) -> torch.Tensor:
