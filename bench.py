@@ -90,6 +90,8 @@ def floor_bytes(stage, B, H, N, d, elem=2) -> float:
         "bwd_dkdv": 6 * t + 2 * rows,        # Q, K, V, dO, LSE*log2e, D in; dK, dV out
         "bwd_dq": 5 * t + 2 * rows,          # Q, K, V, dO, LSE*log2e, D in; dQ out
         "bwd_sparse": 8 * t + 4 * rows,      # the three launches of the sparse backward
+        # E4M3 Q, K, V in (1 byte each); O bf16 and LSE out; the 128-row scales
+        "fwd_fp8": 3 * (t // elem) + t + rows + 2 * 4 * B * H * ((N + 127) // 128) + 4 * B * H,
     }[stage]
 
 
