@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     constexpr int KSTEPS = D / 16;
     constexpr int NQC = BQ / 32;           // 32-query chunks per tile
     constexpr int NDB = D / 32;
-    constexpr int G = D == 64 ? 1 : NQC;   // chunks processed together
+    constexpr int PF = D == 128 ? 2 : KSTEPS;   // S, dP operands loaded ahead of their products
 
     __shared__ __attribute__((aligned(1024))) bf16 q0s[BQ * D];
     __shared__ __attribute__((aligned(1024))) bf16 g0s[BQ * D];
@@ -195,31 +195,41 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         if (!wave_live || (CAUSAL && qbase + BQ - 1 < wk0))
             return;
         const bool need_mask = decltype(masked)::value && qbase < wk0 + 31;
-        // G 32-query chunks at a time (G = 1 at d = 64 keeps the kernel within
-        // 256 registers for two waves per SIMD; G = 2 at d = 128, where the
-        // kernel runs one wave per SIMD and more independent MFMA chains pay):
-        // S, dP, then P and dS, then dV^T += dO^T P and dK^T += Q^T dS
+        // One 32-query chunk at a time: S, dP, then P and dS, then
+        // dV^T += dO^T P and dK^T += Q^T dS.  The S, dP operands are read PF
+        // k-steps ahead of their products (at d = 128 two steps, which keeps
+        // the products' results out of the accumulation registers; at d = 64
+        // all of them first), the group barriers fixing that order.
 #pragma unroll
-        for (int q0c = 0; q0c < NQC; q0c += G) {
+        for (int q0c = 0; q0c < NQC; ++q0c) {
+            constexpr int G = 1;
             f32x16 s[G], dp[G];
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 const int qc = q0c + u;
                 s[u] = f32x16{};
                 dp[u] = f32x16{};
-                // operands first, then the products: keeps the scheduler from
-                // pairing each LDS read with its MFMA (which exposes LDS latency)
                 bf16x8 qa[KSTEPS], ga[KSTEPS];
 #pragma unroll
-                for (int st = 0; st < KSTEPS; ++st) {
+                for (int st = 0; st < PF; ++st) {
                     qa[st] = ld_row8<D>(qt, qc * 32 + l32, st * 16 + hf * 8);
                     ga[st] = ld_row8<D>(gt, qc * 32 + l32, st * 16 + hf * 8);
                 }
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st) {
                     s[u] = mfma_bf16(qa[st], kreg[st], s[u]);
                     dp[u] = mfma_bf16(ga[st], vreg[st], dp[u]);
+                    if (st + PF < KSTEPS) {
+                        qa[st + PF] = ld_row8<D>(qt, qc * 32 + l32, (st + PF) * 16 + hf * 8);
+                        ga[st + PF] = ld_row8<D>(gt, qc * 32 + l32, (st + PF) * 16 + hf * 8);
+                    }
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);          // DS reads
+#pragma unroll
+                for (int st = 0; st < KSTEPS; ++st) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
+                    if (st + PF < KSTEPS)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // DS reads
                 }
             }
             bf16x8 pb[G][2], dsb[G][2];
@@ -423,6 +433,9 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
             // fix the order (reads for step st+2 right after the MFMAs of st)
             f32x16 s = f32x16{}, dp = f32x16{};
             constexpr int PF = 2;
+            // priority up while this wave issues matrix products, so that the
+            // other wave on the SIMD runs its vector work in the gaps
+            __builtin_amdgcn_s_setprio(1);
             bf16x8 ka[KSTEPS], va[KSTEPS];
 #pragma unroll
             for (int st = 0; st < PF; ++st) {
@@ -445,6 +458,7 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
                 if (st + PF < KSTEPS)
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
             }
+            __builtin_amdgcn_s_setprio(0);
             bf16x8 dsb[2];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -461,11 +475,13 @@ __global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_ker
                 for (int hh = 0; hh < 2; ++hh)
                     kta[db][hh] = ld_tr8<D>(kt, kc * 32 + hh * 16, db * 32);
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
                     dq_acc[db] = mfma_bf16(kta[db][hh], dsb[hh], dq_acc[db]);
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 
