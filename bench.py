@@ -510,8 +510,8 @@ def main(argv=None):
         detail["fwd_bwd_tflops_3.5x"] = round(3.5 * fflops / (ms_per_step * 1e-3) / 1e12, 2)
 
     sweep = [int(t) for t in args.tile_sweep.split(",") if t.strip()] if mask is None else []
-    if d == 256:   # key tiles built at head dim 256
-        sweep = [t for t in sweep if t in (32, 64)] or ([32, 64] if args.tile_sweep else [])
+    if d == 256 and sweep:   # the key tiles built at head dim 256
+        sweep = [32, 64]
     if sweep:
         res = {}
         for t in sweep:
