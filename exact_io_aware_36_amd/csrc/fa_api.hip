@@ -11,7 +11,7 @@ namespace {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// d = 256 is built for the bf16 forward passes only (dense and block-sparse)
+// d = 256 is built for the bf16 paths (forward, backward, block-sparse)
 fa_status check_common(const void *q, const void *k, const void *v, int B, int H, int N, int d,
                        float scale, bool allow_256 = false)
 {
@@ -89,7 +89,7 @@ static size_t ws_region(int B, int H, int N) { return ((size_t)B * H * N * sizeo
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d)
 {
-    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128))
+    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128 && d != 256))
         return 0;
     return 2 * ws_region(B, H, N);
 }
@@ -102,7 +102,7 @@ static fa_status check_bwd(const void *q, const void *k, const void *v, const vo
                            const int32_t *kv_lens, fa_dtype dtype, const void *workspace,
                            size_t workspace_bytes)
 {
-    fa_status st = check_common(q, k, v, B, H, N, d, scale);
+    fa_status st = check_common(q, k, v, B, H, N, d, scale, dtype == FA_DTYPE_BF16);
     if (st != FA_OK)
         return st;
     if (!o || !dout || !lse || !dq || !dk || !dv)

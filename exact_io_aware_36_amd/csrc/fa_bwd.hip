@@ -81,14 +81,20 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const bf16 *__restrict__ o
 // Q and dO tiles (and their rows' LSE and D) reach LDS by direct buffer->LDS
 // loads into two stages; the loop is unrolled by two.  Query rows past N read
 // as zeros (Q, dO, LSE, D all 0), which makes their dS and P^T dO terms 0.
-template <int D, bool CAUSAL, bool SPARSE>
+//
+// MODE 0 computes dK and dV together.  At d = 256 the K, V operands and the
+// two accumulators of a wave's 32 keys do not fit one wave's registers, so
+// the work is split over two launches: MODE 1 (dV only: S, P, dV^T += dO^T P)
+// and MODE 2 (dK only: S, dP, dS, dK^T += Q^T dS), recomputing S once more.
+template <int D, bool CAUSAL, bool SPARSE, int MODE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs p, float c_log2)
 {
+    constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
     constexpr int BKV = 128, BQ = 64;
     constexpr int KSTEPS = D / 16;
     constexpr int NQC = BQ / 32;           // 32-query chunks per tile
     constexpr int NDB = D / 32;
-    constexpr int PF = D == 128 ? 2 : KSTEPS;   // S, dP operands loaded ahead of their products
+    constexpr int PF = D >= 128 ? 2 : KSTEPS;   // S, dP operands loaded ahead of their products
 
     __shared__ __attribute__((aligned(1024))) bf16 q0s[BQ * D];
     __shared__ __attribute__((aligned(1024))) bf16 g0s[BQ * D];
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     for (int st = 0; st < KSTEPS; ++st) {
         if (key < N) {
             kreg[st] = *(const bf16x8 *)(K + (size_t)key * D + st * 16 + hf * 8);
-            vreg[st] = *(const bf16x8 *)(V + (size_t)key * D + st * 16 + hf * 8);
+            vreg[st] = DO_DK ? *(const bf16x8 *)(V + (size_t)key * D + st * 16 + hf * 8) : bf16x8{};
         } else {
             kreg[st] = bf16x8{};
             vreg[st] = bf16x8{};
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         dma.issue(grs, qbase, gd, wave);
         if (wave == 0)
             buffer_to_lds4(lrs, ld, lane * 4, qbase * 4);
-        else if (wave == 1)
+        else if (wave == 1 && DO_DK)
             buffer_to_lds4(drs, dd, lane * 4, qbase * 4);
     };
 
@@ -213,23 +219,27 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
 #pragma unroll
                 for (int st = 0; st < PF; ++st) {
                     qa[st] = ld_row8<D>(qt, qc * 32 + l32, st * 16 + hf * 8);
-                    ga[st] = ld_row8<D>(gt, qc * 32 + l32, st * 16 + hf * 8);
+                    if constexpr (DO_DK)
+                        ga[st] = ld_row8<D>(gt, qc * 32 + l32, st * 16 + hf * 8);
                 }
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st) {
                     s[u] = mfma_bf16(qa[st], kreg[st], s[u]);
-                    dp[u] = mfma_bf16(ga[st], vreg[st], dp[u]);
+                    if constexpr (DO_DK)
+                        dp[u] = mfma_bf16(ga[st], vreg[st], dp[u]);
                     if (st + PF < KSTEPS) {
                         qa[st + PF] = ld_row8<D>(qt, qc * 32 + l32, (st + PF) * 16 + hf * 8);
-                        ga[st + PF] = ld_row8<D>(gt, qc * 32 + l32, (st + PF) * 16 + hf * 8);
+                        if constexpr (DO_DK)
+                            ga[st + PF] = ld_row8<D>(gt, qc * 32 + l32, (st + PF) * 16 + hf * 8);
                     }
                 }
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);          // DS reads
+                constexpr int RD = DO_DK ? 2 : 1;   // operand reads and products per k-step
+                __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);         // DS reads
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x008, RD, 0);          // MFMA
                     if (st + PF < KSTEPS)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // DS reads
+                        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);      // DS reads
                 }
             }
             bf16x8 pb[G][2], dsb[G][2];
@@ -239,15 +249,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
                 for (int g = 0; g < 4; ++g) {
                     const int trow = (q0c + u) * 32 + 8 * g + 4 * hf;
                     const f32x4 l4 = *(const f32x4 *)&lt[trow];
-                    const f32x4 d4 = *(const f32x4 *)&dt[trow];
+                    const f32x4 d4 = DO_DK ? *(const f32x4 *)&dt[trow] : f32x4{};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 4 * g + e;
                         float pv = exp2_hw(fmaf(s[u][i], c_log2, -l4[e]));
                         if (need_mask && key > qbase + trow + e)
                             pv = 0.f;
-                        pb[u][i / 8][i % 8] = (bf16)pv;
-                        dsb[u][i / 8][i % 8] = (bf16)(pv * (dp[u][i] - d4[e]));
+                        if constexpr (DO_DV)
+                            pb[u][i / 8][i % 8] = (bf16)pv;
+                        if constexpr (DO_DK)
+                            dsb[u][i / 8][i % 8] = (bf16)(pv * (dp[u][i] - d4[e]));
                     }
                 }
 #pragma unroll
@@ -257,16 +269,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
                 for (int u = 0; u < G; ++u)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        ga[u][hh] = ld_tr8<D>(gt, (q0c + u) * 32 + hh * 16, db * 32);
-                        qa[u][hh] = ld_tr8<D>(qt, (q0c + u) * 32 + hh * 16, db * 32);
+                        if constexpr (DO_DV)
+                            ga[u][hh] = ld_tr8<D>(gt, (q0c + u) * 32 + hh * 16, db * 32);
+                        if constexpr (DO_DK)
+                            qa[u][hh] = ld_tr8<D>(qt, (q0c + u) * 32 + hh * 16, db * 32);
                     }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < G; ++u)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        dv_acc[db] = mfma_bf16(ga[u][hh], pb[u][hh], dv_acc[db]);
-                        dk_acc[db] = mfma_bf16(qa[u][hh], dsb[u][hh], dk_acc[db]);
+                        if constexpr (DO_DV)
+                            dv_acc[db] = mfma_bf16(ga[u][hh], pb[u][hh], dv_acc[db]);
+                        if constexpr (DO_DK)
+                            dk_acc[db] = mfma_bf16(qa[u][hh], dsb[u][hh], dk_acc[db]);
                     }
             }
         }
@@ -317,8 +333,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
                     kv4[e] = (bf16)(dk_acc[db][4 * g + e] * p.scale);
                     vv4[e] = (bf16)dv_acc[db][4 * g + e];
                 }
-                *(bf16x4 *)(dK + db * 32 + 8 * g + 4 * hf) = kv4;
-                *(bf16x4 *)(dV + db * 32 + 8 * g + 4 * hf) = vv4;
+                if constexpr (DO_DK)
+                    *(bf16x4 *)(dK + db * 32 + 8 * g + 4 * hf) = kv4;
+                if constexpr (DO_DV)
+                    *(bf16x4 *)(dV + db * 32 + 8 * g + 4 * hf) = vv4;
             }
     }
 }
@@ -326,7 +344,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
 // dQ: queries outer ---------------------------------------------------------
 // K and V tiles reach LDS by direct buffer->LDS loads into two stages.
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, (D == 128 && !CAUSAL) ? 1 : 2) void bwd_dq_kernel(BwdArgs p, float c_log2)
+__global__ __launch_bounds__(256, (D == 256 || (D == 128 && !CAUSAL)) ? 1 : 2) void bwd_dq_kernel(BwdArgs p, float c_log2)
 {
     constexpr int BR = 128, BC = 64;
     constexpr int KSTEPS = D / 16;
@@ -544,15 +562,27 @@ hipError_t launch_dot(const BwdArgs &a, hipStream_t s)
                            kargs, 0, s);
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
-hipError_t launch_dkdv(const BwdArgs &a, hipStream_t s)
+template <int D, bool CAUSAL, bool SPARSE, int MODE>
+hipError_t launch_dkdv_mode(const BwdArgs &a, hipStream_t s)
 {
     BwdArgs args = a;
     float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     const int n_kb = (a.N + 127) / 128;
-    return hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, CAUSAL, SPARSE>, dim3(a.B * a.H * n_kb),
-                           dim3(256), kargs, 0, s);
+    return hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, CAUSAL, SPARSE, MODE>,
+                           dim3(a.B * a.H * n_kb), dim3(256), kargs, 0, s);
+}
+
+// d = 64, 128: one launch for dK and dV; d = 256: a dV launch and a dK launch
+template <int D, bool CAUSAL, bool SPARSE>
+hipError_t launch_dkdv(const BwdArgs &a, hipStream_t s)
+{
+    if constexpr (D == 256) {
+        hipError_t e = launch_dkdv_mode<D, CAUSAL, SPARSE, 1>(a, s);
+        return e == hipSuccess ? launch_dkdv_mode<D, CAUSAL, SPARSE, 2>(a, s) : e;
+    } else {
+        return launch_dkdv_mode<D, CAUSAL, SPARSE, 0>(a, s);
+    }
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
@@ -593,6 +623,8 @@ hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, bool sparse, B
         return launch_d<64>(a, causal, sparse, stage, s);
     if (d == 128)
         return launch_d<128>(a, causal, sparse, stage, s);
+    if (d == 256)
+        return launch_d<256>(a, causal, sparse, stage, s);
     return hipErrorInvalidValue;
 }
 

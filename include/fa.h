@@ -39,8 +39,8 @@
  *    contents of device buffers (kv_lens values, mask bytes) are not checked:
  *    kv_lens values outside [0, N] are undefined behaviour.
  *  - Supported: d in {64, 128}; dtype BF16 everywhere; dtype FP32 for the
- *    dense forward only.  d = 256 for the bf16 forward passes (fa_fwd,
- *    fa_fwd_ex, fa_fwd_blocksparse): the large head dimension at which the
+ *    dense forward only.  d = 256 for every bf16 attention entry point
+ *    except the split-KV forward: the large head dimension at which the
  *    tiling loosens ("The Attention Matrix You Never Write Down", section
  *    "What it buys, and where the analysis bites").  bf16 tensors are IEEE
  *    bfloat16, rounded to nearest even on store; all accumulation is fp32.

@@ -66,6 +66,7 @@ def test_workspace_bytes(lib):
     assert lib.fa_bwd_workspace_bytes(16, 16, 512, 64) == 2 * 16 * 16 * 512 * 4
     assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
     assert lib.fa_bwd_workspace_bytes(1, 1, 1, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(2, 16, 8192, 256) == 2 * 2 * 16 * 8192 * 4
 
 
 def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, scale=0.125,
@@ -113,7 +114,7 @@ def bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=2, N=256,
     (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(do=None), INVALID),
     (dict(lse=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID),
     (dict(dv=None), INVALID), (dict(N=0), INVALID), (dict(scale=0.0), INVALID),
-    (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dtype=FP32), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED), (dict(d=512), UNSUPPORTED), (dict(dtype=FP32), UNSUPPORTED),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
     (dict(ws=P + 16), WORKSPACE), (dict(dq=MIS), INVALID),
 ])

@@ -66,6 +66,9 @@ WORKLOADS = {
     # the large head dimension at which the pages say the tiling loosens
     "d256_causal": Workload("d256_causal", 2, 16, 8192, 256, "bf16", True, 1007, input_scale=0.5,
                             note="causal forward at head dim 256"),
+    # the same inputs with dO drawn after them, through forward and backward
+    "d256_fwdbwd": Workload("d256_fwdbwd", 2, 16, 8192, 256, "bf16", True, 1007, input_scale=0.5,
+                            backward=True, note="causal forward + backward at head dim 256"),
     # the long-context causal shape through the block-quantised FP8 forward
     # (Q, K rotated with random signs drawn after the mask, seed 1008)
     "long_context_fp8": Workload("long_context_fp8", 1, 16, 16384, 128, "bf16", True, 1008,
