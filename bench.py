@@ -381,6 +381,61 @@ def bench_fp8(args, w, inp, fa, torch):
     return 0
 
 
+def bench_sweep(args, fa, torch):
+    """The metric's range: N = 256 ... 16384 with 16384 tokens per batch
+    (B = 16384 / N), H = 16, d = 64, 128 and 256, causal and not; seeded
+    N(0,1) inputs (x 0.5 for Q, K, V), dO N(0,1).  For each point: the
+    forward alone and forward + backward (dense stages), HIP events over
+    args.steps calls after args.warmup."""
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for d in (64, 128, 256):
+        for N in (256, 512, 1024, 2048, 4096, 8192, 16384):
+            B, H = max(1, 16384 // N), 16
+            inp = workloads.random_qkv(B, H, N, d, seed=2000 + N + d, input_scale=0.5)
+            q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+            ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+            for causal in (False, True):
+                scale = 1.0 / math.sqrt(d)
+
+                def fwd():
+                    fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+
+                def step():
+                    fwd()
+                    fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=causal, scale=scale)
+
+                f = fwd_flops(B, H, N, d, causal)
+                t_f = timed(fwd, args.steps)
+                t_s = timed(step, args.steps)
+                print(json.dumps({
+                    "sweep": "attention fwd / fwd+bwd", "B": B, "H": H, "N": N, "d": d,
+                    "causal": causal, "fwd_ms": round(t_f, 4),
+                    "fwd_tflops": round(f / (t_f * 1e-3) / 1e12, 1),
+                    "fwd_pct_peak": round(100 * f / (t_f * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
+                    "fwd_bwd_ms": round(t_s, 4),
+                    "fwd_bwd_tflops": round(2.5 * f / (t_s * 1e-3) / 1e12, 1)}), flush=True)
+            del q, k, v, do, o, lse, dq, dk, dv, ws
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +447,9 @@ def main(argv=None):
                     help="forward key tiles to time on the side ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the single workload: one JSON line per (N, d, causal) with "
+                         "N = 256..16384, d = 64/128/256, H = 16, B = 16384/N, fwd and fwd+bwd")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="first run one plain device copy of MB MiB (a known-size kernel "
                          "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
@@ -411,6 +469,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.sweep:
+        return bench_sweep(args, fa, torch)
     w = workloads.WORKLOADS[args.workload]
     inp = workloads.make_inputs(w)
     if w.nq is not None:
