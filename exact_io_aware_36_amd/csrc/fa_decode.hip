@@ -116,10 +116,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p)
     auto load = [&](int kb, u32x4 (&kr)[U], u32x4 (&vr)[U]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + (unsigned)((kb + u * RPI) * D * 2), 0, kNT);
+            kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + (unsigned)(kb + u * RPI) * (unsigned)(D * 2), 0, kNT);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + (unsigned)((kb + u * RPI) * D * 2), 0, kNT);
+            vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + (unsigned)(kb + u * RPI) * (unsigned)(D * 2), 0, kNT);
     };
     auto step = [&](int kb, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) __attribute__((always_inline)) {
         // scores and probabilities (kept in pr), one query row at a time

@@ -99,7 +99,10 @@ __device__ __forceinline__ bf16x8 ld_tr8(const bf16 *t, int row0, int col0)
 // predication.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16 *base, int rows, int D)
 {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, rows * D * 2, 0x00020000);
+    // byte count computed unsigned: rows * D * 2 may reach 2^32 - 2 (the
+    // hardware field is 32-bit unsigned)
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0,
+                                            (int)((unsigned)rows * (unsigned)D * 2u), 0x00020000);
 }
 
 // wave index as a scalar, so that branches on it are uniform
@@ -122,7 +125,7 @@ struct TileStage {
         for (int i = 0; i < CH; ++i) {
             const int cidx = threadIdx.x + 256 * i;
             const int row = cidx / CPR, col = (cidx % CPR) * 8;
-            const unsigned off = (unsigned)(((row0 + row) * D + col) * 2);
+            const unsigned off = ((unsigned)(row0 + row) * (unsigned)D + (unsigned)col) * 2u;
             typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
             r[i] = __builtin_bit_cast(bf16x8, v);
@@ -187,7 +190,7 @@ struct TileDma {
     {
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i)
-            buffer_to_lds16(rs, t + (wave + WAVES * i) * 512, voff[i], row0 * D * 2);
+            buffer_to_lds16(rs, t + (wave + WAVES * i) * 512, voff[i], (int)((unsigned)row0 * (unsigned)D * 2u));
     }
 };
 
