@@ -255,7 +255,7 @@ static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits)
 {
-    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0 || (d != 64 && d != 128))
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0 || (d != 64 && d != 128 && d != 256))
         return 0;
     int S, chunk;
     splitkv_plan(B, H, Nk, num_splits, &S, &chunk);
@@ -276,7 +276,7 @@ fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, f
         return FA_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !isfinite(scale))
         return FA_ERR_INVALID_ARG;
-    if (d != 64 && d != 128)
+    if (d != 64 && d != 128 && d != 256)
         return FA_ERR_UNSUPPORTED;
     const int64_t nmax = Nq > Nk ? Nq : Nk;
     if ((int64_t)B * H * nmax * d >= ((int64_t)1 << 31))

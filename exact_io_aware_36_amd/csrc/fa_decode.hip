@@ -15,7 +15,7 @@
 // Foundations, IO-Aware Tiling, Online Softmax, and Recomputation Dynamics",
 // section "Incremental Online Updates", in log-sum-exp form.
 //
-// Lane layout (D = 64 or 128): a key row is D/8 lanes wide, each lane owning
+// Lane layout (D = 64, 128 or 256): a key row is D/8 lanes wide, each lane owning
 // one 16-byte chunk (8 elements); one wave load covers 64/(D/8) consecutive
 // rows (1 KB).  Every group of D/8 lanes keeps its own running max, sum and
 // output accumulator over the rows it loads; the groups of the workgroup are
@@ -38,18 +38,21 @@ __device__ __forceinline__ float dpp(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the LPR lanes (8 or 16, aligned) that hold one key row: lane ^ 1,
-// lane ^ 2 (quad permutes), then the mirrored quad of the 8-lane half row,
-// then (16 lanes) the mirrored half row.  Every lane of the group ends with
-// the full sum.
+// Sum over the LPR lanes (8, 16 or 32, aligned) that hold one key row:
+// lane ^ 1, lane ^ 2 (quad permutes), then the mirrored quad of the 8-lane
+// half row, then (16 lanes) the mirrored half row, then (32 lanes) the other
+// 16-lane row through a lane shuffle.  Every lane of the group ends with the
+// full sum.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x)
 {
     x += dpp<0xB1>(x);      // quad_perm [1, 0, 3, 2]
     x += dpp<0x4E>(x);      // quad_perm [2, 3, 0, 1]
     x += dpp<0x141>(x);     // row_half_mirror
-    if constexpr (LPR == 16)
+    if constexpr (LPR >= 16)
         x += dpp<0x140>(x); // row_mirror
+    if constexpr (LPR == 32)
+        x += __shfl_xor(x, 16);
     return x;
 }
 
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p)
 {
     constexpr int LPR = D / 8;              // lanes per key row
     constexpr int RPI = 64 / LPR;           // key rows per wave load
-    constexpr int KB = NQ >= 4 ? 16 : 32;   // keys per wave step
+    constexpr int KB = (NQ >= 4 || D == 256) ? 16 : 32;   // keys per wave step
     constexpr int U = KB / RPI;             // loads per tensor per step
     constexpr int NG = 4 * RPI;             // row groups per workgroup
     constexpr float TAU = 8.0f;             // lazy rescale threshold (log2 units)
@@ -303,7 +306,11 @@ hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s)
 
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t s)
 {
-    return d == 64 ? launch_decode_d<64>(a, s) : launch_decode_d<128>(a, s);
+    if (d == 64)
+        return launch_decode_d<64>(a, s);
+    if (d == 128)
+        return launch_decode_d<128>(a, s);
+    return launch_decode_d<256>(a, s);
 }
 
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int S, int R, int d, void *o,

@@ -39,8 +39,8 @@
  *    contents of device buffers (kv_lens values, mask bytes) are not checked:
  *    kv_lens values outside [0, N] are undefined behaviour.
  *  - Supported: d in {64, 128}; dtype BF16 everywhere; dtype FP32 for the
- *    dense forward only.  d = 256 for every bf16 attention entry point
- *    except the split-KV forward: the large head dimension at which the
+ *    dense forward only.  d = 256 for every bf16 attention entry point: the
+ *    large head dimension at which the
  *    tiling loosens ("The Attention Matrix You Never Write Down", section
  *    "What it buys, and where the analysis bites").  bf16 tensors are IEEE
  *    bfloat16, rounded to nearest even on store; all accumulation is fp32.
@@ -231,7 +231,7 @@ fa_status fa_bwd_blocksparse(const void *q, const void *k, const void *v, const 
  * A query that sees no key gets O = 0, LSE = -inf.
  * Errors: FA_ERR_INVALID_ARG for null pointers, sizes < 1, num_splits < 0,
  * a non-finite or non-positive scale, misalignment or B*H*max(Nq,Nk)*d >= 2^31;
- * FA_ERR_UNSUPPORTED for d not in {64, 128}, Nq > 8 or dtype other than
+ * FA_ERR_UNSUPPORTED for d not in {64, 128, 256}, Nq > 8 or dtype other than
  * BF16; FA_ERR_WORKSPACE for a missing, small or misaligned workspace.
  */
 int fa_splitkv_splits(int B, int H, int Nk, int num_splits);

@@ -212,7 +212,7 @@ def splitkv(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=1, Nk=100000, d=128, ca
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(o=None), INVALID),
     (dict(lse=None), INVALID), (dict(B=0), INVALID), (dict(Nq=0), INVALID), (dict(Nk=0), INVALID),
     (dict(ns=-1), INVALID), (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
-    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(Nq=9), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED), (dict(d=512), UNSUPPORTED), (dict(Nq=9), UNSUPPORTED),
     (dict(dtype=FP32), UNSUPPORTED),
     (dict(B=64, H=64, Nk=8192), INVALID),                    # B*H*Nk*d >= 2^31
     (dict(q=MIS), INVALID), (dict(v=MIS), INVALID), (dict(lse=P + 2), INVALID),

@@ -48,6 +48,8 @@ CASES = [
     (2, 2, 1, 2048, 128, False, [0, 2048], 0),   # batch 0: empty cache
     (1, 2, 1, 300, 128, False, None, 1000),      # more splits asked than 32-key chunks
     (1, 1, 1, 20000, 64, False, None, 0),        # one (b, h): many splits
+    (2, 2, 1, 1000, 256, False, "rand", 0),      # head dim 256 (32 lanes per key row)
+    (1, 2, 5, 700, 256, True, "rand", 3),
 ]
 
 
