@@ -32,7 +32,10 @@
 // (log2 units); otherwise the tile's exponentials are taken against the old
 // m and may reach 2^8.  The result is unchanged: l and the accumulator share
 // the same reference, and the final division cancels it.  This skips the
-// O(d) rescale of the accumulator on most tiles.
+// O(d) rescale of the accumulator on most tiles.  Since every exponential
+// taken against m is at most the row's partial sum, the tile maximum itself
+// is only computed when that sum passes 2^TAU: most tiles skip the max
+// reduction and give the same result.
 //
 // Tiles in LDS: K and V are both row-major and swizzled (fa_tile.h), copied
 // from HBM by direct buffer->LDS loads.  K is read as the A operand of
@@ -50,13 +53,31 @@
 namespace fa {
 
 constexpr float TAU = 8.f;             // lazy-rescale threshold (log2 units)
+constexpr float kPassLimit = 256.f;    // 2^TAU
+
+// Workgroup barrier that waits for this wave's LDS reads but leaves its
+// buffer->LDS copies in flight (the plain barrier would wait for those too).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_but()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // ---------------------------------------------------------------------------
 // bf16 forward.  D = head dim, BC = keys per tile, BR = 128 queries per
 // workgroup.  SPARSE walks the nonzero 128-blocks of the workgroup's mask row.
 //
-// Tiles reach LDS by direct buffer->LDS loads into two stages; the loop is
-// unrolled by two so each half reads one stage while the other stage fills.
+// Tiles reach LDS by direct buffer->LDS loads into two stages (the loop is
+// unrolled by two so the stage of each access is known at compile time); K
+// and V stages are refilled separately, as soon as the phase reading them is
+// done, two tiles ahead.
 //
 // D = 256 keeps the same schedule: Q's operands (64 registers) and the O^T
 // accumulator (128) need the 512-register budget of one wave per SIMD, and
@@ -135,12 +156,9 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
             qreg[s] = bf16x8{};
     }
 
-    TileDma<BC, D, 4> dma;
+    using Dma = TileDma<BC, D, 4>;
+    Dma dma;
     dma.init(wave);
-    auto issue = [&](int j, bf16 *kd, bf16 *vd) __attribute__((always_inline)) {
-        dma.issue(krs, j * BC, kd, wave);
-        dma.issue(vrs, j * BC, vd, wave);
-    };
 
     float m = -INFINITY;   // reference max (log2 units), same in both lane halves
     float lsum = 0.f;      // running sum, partial over this lane half's keys
@@ -149,16 +167,14 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
     for (int db = 0; db < NDB; ++db)
         oacc[db] = f32x16{};
 
-    // MASKED instances handle the trailing tiles that cross the causal
-    // diagonal or the key length; the main loop runs the unmasked instance
-    auto compute = [&](auto masked, int j, const bf16 *kt, const bf16 *vt) __attribute__((always_inline)) {
-        const int kbase = j * BC;
+    f32x16 s[NKC];         // S^T of the current tile, between its two phases
+
+    // phase 1 of tile j: S^T = K_j Q^T
+    auto compute_s = [&](int j, const bf16 *kt) __attribute__((always_inline)) {
         // whole tile above this wave's diagonal: nothing to add
-        if (CAUSAL && kbase > wq0 + 31)
+        if (CAUSAL && j * BC > wq0 + 31)
             return;
-        // S^T = K_j Q^T
         // operands first, then the products (keeps LDS latency off each MFMA)
-        f32x16 s[NKC];
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
             bf16x8 ka[KSTEPS];
@@ -171,7 +187,14 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
             for (int st = 0; st < KSTEPS; ++st)
                 s[kc] = mfma_bf16(ka[st], qreg[st], s[kc]);
         }
-        // masks: only tiles that cross the diagonal or the key length
+    };
+    // phase 2 of tile j: masks, softmax, O^T += V_j^T P^T.  MASKED instances
+    // handle the trailing tiles that cross the causal diagonal or the key
+    // length; the main loop runs the unmasked instance.
+    auto compute_pv = [&](auto masked, int j, const bf16 *vt) __attribute__((always_inline)) {
+        const int kbase = j * BC;
+        if (CAUSAL && kbase > wq0 + 31)
+            return;
         if (decltype(masked)::value && ((kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0))) {
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
@@ -182,35 +205,56 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
                         s[kc][i] = -INFINITY;
                 }
         }
-        // tile max; move the reference only when it grows past TAU
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                mx = fmaxf(mx, s[kc][i]);
-        const float mt = pair_max(mx) * c_log2;
-        if (__any(mt > m + TAU)) {
-            const float m_new = fmaxf(m, mt);
-            const float alpha = exp2_hw(m - m_new);   // 0 when m = -inf
-            m = m_new;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                oacc[db] *= alpha;
-        }
-        const float m_use = (m == -INFINITY) ? 0.f : m;
-        // probabilities (fp32 row sum), bf16 operands for P V
+        // Probabilities against the current reference m, with fp32 row sums
+        // and bf16 operands for P V.  The reference must move (lazily: only
+        // when the tile's maximum exceeds it by more than TAU) exactly when
+        // some probability would pass 2^TAU, and every probability is at
+        // most the lane's row sum, so the tile maximum is needed only when a
+        // partial row sum passes 2^TAU (or the row has no reference yet):
+        // the common tile skips the max reduction.  Either way the result is
+        // the one the max-first order gives.
         float rs = 0.f;
         bf16x8 pb[NKC][2];
+        bool slow = __any(m == -INFINITY);
+        if (!slow) {
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
+            for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m_use));
-                rs += pv;
-                pb[kc][i / 8][i % 8] = (bf16)pv;
+                for (int i = 0; i < 16; ++i) {
+                    const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m));
+                    rs += pv;
+                    pb[kc][i / 8][i % 8] = (bf16)pv;
+                }
+            slow = __any(!(rs <= kPassLimit));   // also catches inf
+        }
+        if (slow) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, s[kc][i]);
+            const float mt = pair_max(mx) * c_log2;
+            if (__any(mt > m + TAU)) {
+                const float m_new = fmaxf(m, mt);
+                const float alpha = exp2_hw(m - m_new);   // 0 when m = -inf
+                m = m_new;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] *= alpha;
             }
+            const float m_use = (m == -INFINITY) ? 0.f : m;
+            rs = 0.f;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m_use));
+                    rs += pv;
+                    pb[kc][i / 8][i % 8] = (bf16)pv;
+                }
+        }
         lsum += rs;
         // O^T += V_j^T P^T
 #pragma unroll
@@ -230,20 +274,29 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
         }
     };
 
-    // one step = two tiles, one per LDS stage
-    auto step = [&](auto masked, int t) __attribute__((always_inline)) {
-        if (t + 1 < n_tiles)
-            issue(tile_of(t + 1), k1s, v1s);
-        compute(masked, tile_of(t), k0s, v0s);
-        wait_vmem();
-        __syncthreads();
-        if (t + 1 < n_tiles) {
-            if (t + 2 < n_tiles)
-                issue(tile_of(t + 2), k0s, v0s);
-            compute(masked, tile_of(t + 1), k1s, v1s);
-            wait_vmem();
-            __syncthreads();
-        }
+    // Tile t (LDS stage ST = t & 1) in two phases separated by a barrier, so
+    // that K and V stages free up at different times: K_{t+2} is copied into
+    // K_t's stage once every wave has finished S_t (barrier A), and V_{t+2}
+    // into V_t's stage once every wave has finished P V (barrier B).  Each
+    // copy then has about one and a half tiles of compute to land before its
+    // wait, which lets the two copies issued since stay in flight.  Every
+    // tile issues both copies (past the last tile, duplicates of it into a
+    // free stage), so the in-flight count is fixed.
+    constexpr int kCopies = 2 * Dma::PER_WAVE;  // loads of the two newest copies
+    auto tile = [&](auto masked, int t, auto st_c) __attribute__((always_inline)) {
+        constexpr int ST = decltype(st_c)::value;
+        bf16 *kt = ST ? k1s : k0s;
+        bf16 *vt = ST ? v1s : v0s;
+        const int j = tile_of(t);
+        const int j2 = tile_of(min(t + 2, n_tiles - 1));
+        compute_s(j, kt);
+        wait_vmem_but<kCopies>();                // V_t has landed
+        lds_barrier();                           // A
+        dma.issue(krs, j2 * BC, kt, wave);
+        compute_pv(masked, j, vt);
+        wait_vmem_but<kCopies>();                // K_{t+1} has landed
+        lds_barrier();                           // B
+        dma.issue(vrs, j2 * BC, vt, wave);
     };
     // leading tiles that no wave needs to mask: whole tiles below the key
     // length and (causal) entirely at or left of the block's first query
@@ -254,14 +307,27 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
             n_plain = min(n_plain, (q0 + 1) / BC);
     }
     const int t_mask = n_plain & ~1;
-    if (n_tiles > 0)
-        issue(tile_of(0), k0s, v0s);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (n_tiles > 0) {
+        const int j1 = tile_of(min(1, n_tiles - 1));
+        dma.issue(krs, tile_of(0) * BC, k0s, wave);
+        dma.issue(vrs, tile_of(0) * BC, v0s, wave);
+        dma.issue(krs, j1 * BC, k1s, wave);
+        dma.issue(vrs, j1 * BC, v1s, wave);
+    }
     wait_vmem();
     __syncthreads();
-    for (int t = 0; t < t_mask; t += 2)
-        step(std::false_type{}, t);
-    for (int t = t_mask; t < n_tiles; t += 2)
-        step(std::true_type{}, t);
+    for (int t = 0; t < t_mask; t += 2) {
+        tile(std::false_type{}, t, I0{});
+        tile(std::false_type{}, t + 1, I1{});
+    }
+    for (int t = t_mask; t < n_tiles; t += 2) {
+        tile(std::true_type{}, t, I0{});
+        if (t + 1 < n_tiles)
+            tile(std::true_type{}, t + 1, I1{});
+    }
+    wait_vmem();
 
     // ---- epilogue: O = acc / l, LSE = ln2 (m + log2 l)
     const float ltot = pair_sum(lsum);
