@@ -31,6 +31,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kE4M3Max = 448.f;
 constexpr float TAU8 = 8.f;     // lazy-rescale threshold (log2 units)
+constexpr float kPassLimit8 = 256.f;   // 2^TAU8
 
 // ---------------------------------------------------------------------------
 // Quantiser.  One workgroup (256 threads) per 128-row block of one (b, h).
@@ -412,41 +413,56 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdArgs p)
                         s[kc][i] = -INFINITY;
                 }
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                mx = fmaxf(mx, s[kc][i]);
-        const float mt = pair_max(mx) * c_t;
-        if (__any(mt > m + TAU8)) {
-            const float m_new = fmaxf(m, mt);
-            const float alpha = exp2_hw(m - m_new);
-            m = m_new;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                oacc[db] *= alpha;
-        }
-        const float m_use = (m == -INFINITY) ? 0.f : m;
         // probabilities: fp32 row sum, E4M3 operand bytes (slot 16 kc + i)
-        float rs = 0.f;
         int pw[8];
+        auto probs = [&](float m_ref) __attribute__((always_inline)) -> float {
+            float acc = 0.f;
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
+            for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-            for (int i = 0; i < 16; i += 4) {
-                float pv[4];
+                for (int i = 0; i < 16; i += 4) {
+                    float pv[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pv[e] = exp2_hw(fmaf(s[kc][i + e], c_t, -m_use));
-                    rs += pv[e];
+                    for (int e = 0; e < 4; ++e) {
+                        pv[e] = exp2_hw(fmaf(s[kc][i + e], c_t, -m_ref));
+                        acc += pv[e];
+                    }
+                    int wd = 0;
+                    wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], wd, false);
+                    wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
+                    pw[(16 * kc + i) / 4] = wd;
                 }
-                int wd = 0;
-                wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], wd, false);
-                wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
-                pw[(16 * kc + i) / 4] = wd;
+            return acc;
+        };
+        // Against the current reference first: every probability is at most
+        // the lane's partial row sum, so while no partial sum passes 2^TAU
+        // the lazy rule would not move the reference and the tile maximum is
+        // not needed (same result as taking it first).
+        float rs = 0.f;
+        bool slow = __any(m == -INFINITY);
+        if (!slow) {
+            rs = probs(m);
+            slow = __any(!(rs <= kPassLimit8));   // also catches inf
+        }
+        if (slow) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, s[kc][i]);
+            const float mt = pair_max(mx) * c_t;
+            if (__any(mt > m + TAU8)) {
+                const float m_new = fmaxf(m, mt);
+                const float alpha = exp2_hw(m - m_new);
+                m = m_new;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] *= alpha;
             }
+            rs = probs((m == -INFINITY) ? 0.f : m);
+        }
         lsum += rs;
         const i32x8 pop = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
         // O^T += V^T P^T
