@@ -110,12 +110,15 @@ def flash_io_elements(N, d, M) -> float:
 
 # ---------------------------------------------------------------------------
 
-KERNEL_HEADERS = ("exact_io_aware_36_amd/csrc/fa_tile.h", "exact_io_aware_36_amd/csrc/fa_internal.h")
+# what else decides a kernel's machine code: the two headers every kernel
+# includes and the build script that holds the compiler flags
+KERNEL_HEADERS = ("exact_io_aware_36_amd/csrc/fa_tile.h", "exact_io_aware_36_amd/csrc/fa_internal.h",
+                  "exact_io_aware_36_amd/build.py")
 
 
 def source_digest(path: str) -> str:
     """First 16 hex digits of the sha256 over the kernel source followed by the
-    two headers every kernel includes."""
+    two headers every kernel includes and the build script (compiler flags)."""
     h = hashlib.sha256()
     for p in (path,) + KERNEL_HEADERS:
         with open(os.path.join(ROOT, p), "rb") as f:

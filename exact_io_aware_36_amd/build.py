@@ -3,6 +3,13 @@
 Every HIP source is compiled for gfx950 with packed-fp32 instructions
 disabled (-packed-fp32-ops) and code-object version 5; the objects are linked
 into exact_io_aware_36_amd/libfa.so next to this file.
+
+MFMA results are kept in ordinary vector registers (-amdgpu-mfma-vgpr-form).
+Without it, a kernel allowed the full 512-register budget (one wave per SIMD)
+gets its MFMA accumulators in the accumulation registers, and every score
+tile the softmax reads then needs one copy instruction per register; with it
+the compiler uses those registers only as spill space.  Measured: the d = 256
+forward 12 % faster, the backward kernels 1-2 % faster, identical output.
 """
 from __future__ import annotations
 
@@ -22,7 +29,8 @@ ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-ffp-contract=fast", "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
+    "-ffp-contract=fast", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
 
 
