@@ -119,3 +119,21 @@ def test_fwd_fp8_score_patterns(fa, kind, causal):
     bound = ofp8.p_quant_bound(Q, K, V, L, causal=causal, kv_lens=None)
     check_bound("O", o, O, bound)
     check_lse("LSE", lse, L)
+
+
+@pytest.mark.parametrize("kind", ["ramp", "plateau", "falling", "spike"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_splitkv_score_patterns(fa, kind, d):
+    """The split-KV decode kernel keeps its own running maxima per lane group
+    and per split; the same profiles over a 5000-key cache, three query rows
+    (causal), default and single-split plans."""
+    B, H, Nk, Nq = 1, 2, 5000, 3
+    inp = pattern_qkv(kind, B, H, Nk, d, 3200 + d + len(kind))
+    q = inp["q"][:, :, -Nq:].contiguous()
+    O, L = oracle.decode(f64(q), f64(inp["k"]), f64(inp["v"]), causal=True, scale=1.0 / math.sqrt(d))
+    for ns in (0, 1):
+        say(f"  decode {kind} d={d} Nk={Nk} Nq={Nq} splits={fa.fa_splitkv_splits(B, H, Nk, ns)}")
+        o, lse = fa.fwd_splitkv(q.cuda(), inp["k"].cuda(), inp["v"].cuda(), causal=True, num_splits=ns)
+        torch.cuda.synchronize()
+        check_bf16("O", host(o), O)
+        check_lse("LSE", host(lse), L)
