@@ -137,3 +137,63 @@ def test_splitkv_score_patterns(fa, kind, d):
         torch.cuda.synchronize()
         check_bf16("O", host(o), O)
         check_lse("LSE", host(lse), L)
+
+
+def rounding_bounds(q, k, v, do, O, L, causal, scale):
+    """First-order bounds on the gradients' errors from the bf16 roundings
+    in the path (at most 2^-8 relative per element -- half an ulp of an
+    8-bit significand -- doubled for the fp32 work around them, hence 2^-7):
+    the fp32 operands P of dV = P^T dO and dS = P (dP - D) of dQ = scale dS K
+    and dK = scale dS^T Q, and the stored bf16 O that D_i = dO_i . O_i is
+    computed from (|dD_i| <= 2^-7 sum_d |do_id o_id|, entering dS as
+    P_ij dD_i):
+      dV: sum_i P_ij |do_id| 2^-7
+      dQ: scale sum_j (|dS_ij| 2^-7 + P_ij |dD_i|) |k_jd|
+      dK: scale sum_i (|dS_ij| 2^-7 + P_ij |dD_i|) |q_id|.
+    With keys of large norm along one direction these are not small against
+    the gradients: dQ's component along it is a sum of large terms that
+    cancel (sum_j dS_ij = 0 for every row), and the softmax of every row
+    piles onto the same few keys."""
+    B, H, N, d = q.shape
+    bq, bk, bv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            if causal:
+                s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+            P = np.exp(s - L[b, h][:, None])
+            dP = do[b, h] @ v[b, h].T
+            D = (P * dP).sum(axis=1)
+            dD = (np.abs(do[b, h]) * np.abs(O[b, h])).sum(axis=1) * 2.0 ** -7
+            w = np.abs(P * (dP - D[:, None])) * 2.0 ** -7 + P * dD[:, None]
+            bq[b, h] = scale * (w @ np.abs(k[b, h]))
+            bk[b, h] = scale * (w.T @ np.abs(q[b, h]))
+            bv[b, h] = (P.T @ np.abs(do[b, h])) * 2.0 ** -7
+    return bq, bk, bv
+
+
+@pytest.mark.parametrize("kind", ["ramp", "spike"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_score_patterns(fa, kind, d, causal):
+    """The backward recomputes P = 2^(S c - LSE) from the forward's LSE; with
+    scores up to 120 log2 units the difference is taken near 83 in natural
+    units, so this checks that its fp32 cancellation costs nothing beyond the
+    rounding of the products' bf16 operands (the usual absolute bars do not
+    apply to gradients this large and this ill-conditioned)."""
+    B, H, N = 1, 2, 600
+    say(f"  bwd {kind} d={d} causal={causal} N={N}")
+    inp = pattern_qkv(kind, B, H, N, d, 3300 + d + 2 * len(kind) + causal)
+    gen = torch.Generator().manual_seed(3400 + d)
+    do = torch.randn((B, H, N, d), generator=gen).to(torch.bfloat16)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=causal)
+    dq, dk, dv = fa.bwd(q, k, v, o, do.cuda(), lse, causal=causal)
+    torch.cuda.synchronize()
+    Q, K, V, dO = f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(do)
+    dQ, dK, dV, _ = oracle.bwd(Q, K, V, dO, causal=causal)
+    O, L = oracle.fwd(Q, K, V, causal=causal)
+    bq, bk, bv = rounding_bounds(Q, K, V, dO, O, L, causal, 1.0 / math.sqrt(d))
+    check_bound("dQ", host(dq), dQ, bq)
+    check_bound("dK", host(dk), dK, bk)
+    check_bound("dV", host(dv), dV, bv)
