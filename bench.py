@@ -46,9 +46,9 @@ HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 KERNEL_SOURCES = {
     "fwd": "exact_io_aware_36_amd/csrc/fa_fwd.hip",
     "bwd_dot": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
-    "bwd_dkdv": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
+    "bwd_dkdv": "exact_io_aware_36_amd/csrc/fa_bwd_dkdv.hip",
     "bwd_dq": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
-    "bwd_sparse": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
+    "bwd_sparse": ("exact_io_aware_36_amd/csrc/fa_bwd.hip", "exact_io_aware_36_amd/csrc/fa_bwd_dkdv.hip"),
     "decode": "exact_io_aware_36_amd/csrc/fa_decode.hip",
     "fwd_fp8": "exact_io_aware_36_amd/csrc/fa_fp8.hip",
 }
@@ -116,11 +116,13 @@ KERNEL_HEADERS = ("exact_io_aware_36_amd/csrc/fa_tile.h", "exact_io_aware_36_amd
                   "exact_io_aware_36_amd/build.py")
 
 
-def source_digest(path: str) -> str:
-    """First 16 hex digits of the sha256 over the kernel source followed by the
-    two headers every kernel includes and the build script (compiler flags)."""
+def source_digest(path) -> str:
+    """First 16 hex digits of the sha256 over the kernel source (one path, or
+    a tuple of them for a stage spanning several files) followed by the two
+    headers every kernel includes and the build script (compiler flags)."""
     h = hashlib.sha256()
-    for p in (path,) + KERNEL_HEADERS:
+    paths = (path,) if isinstance(path, str) else tuple(path)
+    for p in paths + KERNEL_HEADERS:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

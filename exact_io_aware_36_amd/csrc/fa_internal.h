@@ -38,6 +38,8 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, int tile_n, bool causal, boo
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, bool sparse, hipStream_t s);
 enum class BwdStage { Dot, DkDv, Dq };
+// the dK, dV launch(es) of the backward (fa_bwd_dkdv.hip)
+hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, bool causal, bool sparse, hipStream_t s);
 hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, bool sparse, BwdStage stage,
                             hipStream_t s);
 
