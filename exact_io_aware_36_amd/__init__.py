@@ -94,6 +94,10 @@ _lib.fa_quantize_fp8.restype = _i
 _lib.fa_quantize_fp8.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _sz, _vp]
 _lib.fa_fwd_fp8.restype = _i
 _lib.fa_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp]
+_lib.fa_fwd_kvouter_workspace_bytes.restype = _sz
+_lib.fa_fwd_kvouter_workspace_bytes.argtypes = [_i, _i, _i, _i]
+_lib.fa_fwd_kvouter.restype = _i
+_lib.fa_fwd_kvouter.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]
 _lib.fa_merge.restype = _i
 _lib.fa_merge.argtypes = [_vp, _vp, _i, _i, _i, _vp, _vp, _i, _vp]
 
@@ -419,6 +423,33 @@ def quantize_fp8(x, block_rows=128, signs=None, transpose=False, stream=None):
     return x8, descale
 
 
+def fa_fwd_kvouter_workspace_bytes(B, H, N, d):
+    return int(_lib.fa_fwd_kvouter_workspace_bytes(int(B), int(H), int(N), int(d)))
+
+
+def fa_fwd_kvouter(q, k, v, o, lse, workspace, causal=False, scale=None, stream=None):
+    """The key/value-outer loop order (IO ablation): same outputs as fa_fwd."""
+    B, H, N, d = _shape(q)
+    _same(q, k, v, o)
+    _require(q.dtype == torch.bfloat16, "the key/value-outer forward is bf16 only")
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * N,
+             "lse must be contiguous fp32 [B, H, N]")
+    rc = _lib.fa_fwd_kvouter(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                             int(bool(causal)), _scale(scale, d), _ptr(workspace),
+                             _ws_bytes(workspace), _stream(q, stream))
+    _check_rc(rc, "fa_fwd_kvouter")
+
+
+def fwd_kvouter(q, k, v, causal=False, scale=None, stream=None):
+    """Key/value-outer forward with its own workspace; return (O, LSE)."""
+    B, H, N, d = _shape(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    nbytes = fa_fwd_kvouter_workspace_bytes(B, H, N, d)
+    _require(nbytes > 0, "unsupported size for the key/value-outer forward")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    fa_fwd_kvouter(q, k, v, o, lse, ws, causal=causal, scale=scale, stream=stream)
+    return o, lse
 def fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, causal=False, scale=None, kv_lens=None,
             stream=None):
     """FP8 forward on quantised inputs; return (O bf16 [B, H, N, d], LSE)."""

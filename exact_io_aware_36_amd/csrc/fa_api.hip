@@ -371,4 +371,34 @@ fa_status fa_fwd_fp8(const void *q8, const void *k8, const void *v8t, const floa
                                        N, d, causal != 0, scale, kv_lens, (hipStream_t)stream));
 }
 
+// Key/value-outer forward (the IO ablation).  Workspace: fp32 O accumulator
+// [B][H][N][d], then m and l fp32 [B][H][N], each rounded up to 256 B.
+size_t fa_fwd_kvouter_workspace_bytes(int B, int H, int N, int d)
+{
+    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128))
+        return 0;
+    if ((int64_t)B * H * N * d >= ((int64_t)1 << 31))
+        return 0;
+    return ((size_t)B * H * N * d * sizeof(float) + 255) / 256 * 256 + 2 * ws_region(B, H, N);
+}
+
+fa_status fa_fwd_kvouter(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                         int H, int N, int d, int causal, float scale, void *workspace,
+                         size_t workspace_bytes, fa_stream_t stream)
+{
+    fa_status st = check_common(q, k, v, B, H, N, d, scale);
+    if (st != FA_OK)
+        return st;
+    if (!o || !lse || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_INVALID_ARG;
+    const size_t need = fa_fwd_kvouter_workspace_bytes(B, H, N, d);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return FA_ERR_WORKSPACE;
+    float *o_acc = (float *)workspace;
+    float *m = (float *)((char *)workspace + ((size_t)B * H * N * d * sizeof(float) + 255) / 256 * 256);
+    float *l = (float *)((char *)m + ws_region(B, H, N));
+    fa::KvOuterArgs a{q, k, v, o, lse, o_acc, m, l, B, H, N, scale};
+    return from_hip(fa::launch_fwd_kvouter(a, d, causal != 0, (hipStream_t)stream));
+}
+
 } // extern "C"

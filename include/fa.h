@@ -307,6 +307,33 @@ fa_status fa_fwd_fp8(const void *q8, const void *k8, const void *v8t, const floa
                      int H, int N, int d, int causal, float scale, const int32_t *kv_lens,
                      fa_stream_t stream);
 
+/*
+ * The key/value-outer loop order, kept as an IO ablation of the forward
+ * ("FlashAttention: Mathematical Foundations, IO-Aware Tiling, Online
+ * Softmax, and Recomputation Dynamics", section "IO-Aware Tiling Algorithm";
+ * "01 · FlashAttention", step 5, the HBM accounting).  The outer loop walks
+ * 64-key blocks (one launch each) and the inner loop 128-row query blocks, so
+ * every query block's fp32 output accumulator and running statistics go
+ * through device memory once per key block.  Same results as fa_fwd (exact
+ * attention, O bf16 and LSE as in the conventions above; no kv_lens); it is
+ * not a fast path.
+ *
+ * fa_fwd_kvouter_workspace_bytes: bytes of the workspace, or 0 for
+ * unsupported sizes: fp32 O accumulator [B][H][N][d] followed by two fp32
+ * [B][H][N] statistics, each rounded up to 256 bytes.
+ * fa_fwd_kvouter: arguments as fa_fwd (bf16 only), plus the workspace
+ * (256-byte aligned, at least the size above; its contents on entry do not
+ * matter and are overwritten).
+ * Errors: FA_ERR_INVALID_ARG for null pointers, sizes < 1, a non-finite or
+ * non-positive scale, B*H*N*d >= 2^31, misalignment; FA_ERR_UNSUPPORTED for
+ * d not in {64, 128}; FA_ERR_WORKSPACE for a missing, small or misaligned
+ * workspace.
+ */
+size_t fa_fwd_kvouter_workspace_bytes(int B, int H, int N, int d);
+fa_status fa_fwd_kvouter(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                         int H, int N, int d, int causal, float scale, void *workspace,
+                         size_t workspace_bytes, fa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -273,3 +273,28 @@ def fwd8(lib, q=P, k=P, v=P, qs=P, ks=P, vs=P, o=P, lse=P, B=1, H=1, N=256, d=12
 ])
 def test_fwd_fp8_rejects(lib, kw, want):
     assert fwd8(lib, **kw) == want
+
+
+def test_kvouter_workspace(lib):
+    # fp32 O accumulator, then two fp32 [B, H, N] statistics, each rounded up to 256 bytes
+    assert lib.fa_fwd_kvouter_workspace_bytes(1, 16, 8192, 128) == 16 * 8192 * 128 * 4 + 2 * 16 * 8192 * 4
+    assert lib.fa_fwd_kvouter_workspace_bytes(1, 1, 3, 64) == 768 + 2 * 256
+    assert lib.fa_fwd_kvouter_workspace_bytes(1, 1, 1, 256) == 0
+    assert lib.fa_fwd_kvouter_workspace_bytes(0, 1, 1, 64) == 0
+    assert lib.fa_fwd_kvouter_workspace_bytes(1, 1, 1 << 24, 128) == 0   # B*H*N*d >= 2^31
+
+
+def kvouter(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, scale=0.125,
+            ws=P, wsb=1 << 30):
+    return lib.fa_fwd_kvouter(q, k, v, o, lse, B, H, N, d, causal, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(lse=None), INVALID),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(q=MIS), INVALID), (dict(o=MIS), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE), (dict(ws=MIS), WORKSPACE),
+])
+def test_kvouter_rejects(lib, kw, want):
+    assert kvouter(lib, **kw) == want
