@@ -108,6 +108,25 @@ def flash_io_elements(N, d, M) -> float:
     return 4.0 * N * d + 2.0 * N * N * d * d / M
 
 
+def kvouter_bytes(B, H, N, d, causal) -> float:
+    """Algorithmic HBM bytes of one fa_fwd_kvouter call (the key/value-outer
+    loop order): per 64-key block j, every 128-row query block that sees it
+    reads its Q rows (bf16) and, from the second block on, its fp32 O
+    accumulator and the two fp32 statistics, then writes them back; K_j and
+    V_j count once; a last pass reads the accumulator and statistics and
+    writes O (bf16) and LSE."""
+    tc = (N + 63) // 64
+    total = 0.0
+    for qb in range((N + 127) // 128):
+        rows = min(128, N - 128 * qb)
+        n_j = min(tc, (128 * qb + 127) // 64 + 1) if causal else tc
+        per = rows * d * 2 + rows * d * 4 + 8 * rows          # Q in, O and m, l out
+        total += n_j * per + (n_j - 1) * (rows * d * 4 + 8 * rows)   # reads after block 0
+    total += 2 * N * d * 2                                     # K, V once
+    total += N * d * 4 + 8 * N + N * d * 2 + 4 * N             # the last pass
+    return B * H * total
+
+
 # ---------------------------------------------------------------------------
 
 # what else decides a kernel's machine code: the two headers every kernel
@@ -441,6 +460,60 @@ def bench_sweep(args, fa, torch):
     return 0
 
 
+def bench_io_ablation(args, fa, torch):
+    """The loop-order ablation: for N = 2048, 4096, 8192 (d = 128, H = 16,
+    B = 1, non-causal, seeded N(0,1) inputs x 0.5) the forward (queries
+    outer, O and the statistics in registers) against fa_fwd_kvouter (keys
+    outer, O and the statistics through HBM once per 64-key block), with
+    each one's algorithmic HBM bytes and the pages' element counts for the
+    same N (M = 65536 elements on chip)."""
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    d, H, B = 128, 16, 1
+    for N in (2048, 4096, 8192):
+        inp = workloads.random_qkv(B, H, N, d, seed=2500 + N, input_scale=0.5, with_dout=False)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_fwd_kvouter_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        t_q = timed(lambda: fa.fa_fwd(q, k, v, o, lse, causal=False), args.steps)
+        t_k = timed(lambda: fa.fa_fwd_kvouter(q, k, v, o, lse, ws, causal=False), max(2, args.steps // 4))
+        f = fwd_flops(B, H, N, d, False)
+        print(json.dumps({
+            "io_ablation": "forward loop order", "B": B, "H": H, "N": N, "d": d, "causal": False,
+            "queries_outer_ms": round(t_q, 4), "keys_outer_ms": round(t_k, 4),
+            "queries_outer_tflops": round(f / (t_q * 1e-3) / 1e12, 1),
+            "keys_outer_tflops": round(f / (t_k * 1e-3) / 1e12, 1),
+            "queries_outer_floor_bytes": floor_bytes("fwd", B, H, N, d),
+            "keys_outer_model_bytes": kvouter_bytes(B, H, N, d, False),
+            "page_standard_elements_per_head": standard_io_elements(N, d),
+            "page_tiled_elements_per_head_m65536": flash_io_elements(N, d, 65536)}), flush=True)
+        del q, k, v, o, lse, ws
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,6 +528,9 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the single workload: one JSON line per (N, d, causal) with "
                          "N = 256..16384, d = 64/128/256, H = 16, B = 16384/N, fwd and fwd+bwd")
+    ap.add_argument("--io-ablation", action="store_true",
+                    help="instead of the single workload: the forward against the key/value-outer "
+                         "loop order (fa_fwd_kvouter) at N = 2048, 4096, 8192, d = 128")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="first run one plain device copy of MB MiB (a known-size kernel "
                          "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
@@ -476,6 +552,8 @@ def main(argv=None):
         return 1
     if args.sweep:
         return bench_sweep(args, fa, torch)
+    if args.io_ablation:
+        return bench_io_ablation(args, fa, torch)
     w = workloads.WORKLOADS[args.workload]
     inp = workloads.make_inputs(w)
     if w.nq is not None:

@@ -68,3 +68,24 @@ def test_floor_bytes():
 def test_gpus_above_one_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_kvouter_bytes_closed_form():
+    """The key/value-outer byte model against its closed form when N is a
+    multiple of 128 (every query block full): per head, T_c = N/64 blocks,
+    each moving Q (2 B) and O, l, m out (4 d + 8 B per row), the blocks after
+    the first also reading O, l, m back; K, V once; the last pass."""
+    for N, d in ((1024, 64), (8192, 128)):
+        tc = N // 64
+        per_head = (tc * (2 * N * d + 4 * N * d + 8 * N) + (tc - 1) * (4 * N * d + 8 * N)
+                    + 4 * N * d + (4 * N * d + 8 * N + 2 * N * d + 4 * N))
+        assert bench.kvouter_bytes(2, 3, N, d, False) == 6 * per_head
+
+
+def test_kvouter_bytes_grows_quadratically_and_causal_halves():
+    r = bench.kvouter_bytes(1, 1, 16384, 128, False) / bench.kvouter_bytes(1, 1, 8192, 128, False)
+    assert 3.9 < r < 4.0
+    c = bench.kvouter_bytes(1, 1, 8192, 128, True) / bench.kvouter_bytes(1, 1, 8192, 128, False)
+    assert 0.5 < c < 0.52
+    # against the queries-outer floor: two orders of magnitude at N = 8192
+    assert bench.kvouter_bytes(1, 16, 8192, 128, False) > 100 * bench.floor_bytes("fwd", 1, 16, 8192, 128)
