@@ -6,6 +6,7 @@
 
 #include "fa.h"
 #include "fa_internal.h"
+#include "fa_kvouter.h"
 
 namespace {
 

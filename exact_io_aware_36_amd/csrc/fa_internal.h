@@ -38,18 +38,6 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, int tile_n, bool causal, boo
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, bool sparse, hipStream_t s);
 enum class BwdStage { Dot, DkDv, Dq };
-// Key/value-outer forward (the IO ablation): fp32 O accumulator and running
-// statistics m (log2 units), l in the workspace, [B][H][N][D] and [B][H][N].
-struct KvOuterArgs {
-    const void *q, *k, *v;
-    void *o;
-    float *lse;
-    float *o_acc, *m, *l;
-    int B, H, N;
-    float scale;
-};
-hipError_t launch_fwd_kvouter(const KvOuterArgs &a, int d, bool causal, hipStream_t s);
-
 // the dK, dV launch(es) of the backward (fa_bwd_dkdv.hip)
 hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, bool causal, bool sparse, hipStream_t s);
 hipError_t launch_bwd_stage(const BwdArgs &a, int d, bool causal, bool sparse, BwdStage stage,

@@ -22,6 +22,7 @@
 #include <math.h>
 
 #include "fa_internal.h"
+#include "fa_kvouter.h"
 #include "fa_tile.h"
 
 namespace fa {
