@@ -139,7 +139,7 @@ def test_splitkv_score_patterns(fa, kind, d):
         check_lse("LSE", host(lse), L)
 
 
-def rounding_bounds(q, k, v, do, O, L, causal, scale):
+def rounding_bounds(q, k, v, do, O, L, causal, scale, kv_lens=None):
     """First-order bounds on the gradients' errors from the bf16 roundings
     in the path (at most 2^-8 relative per element -- half an ulp of an
     8-bit significand -- doubled for the fp32 work around them, hence 2^-7):
@@ -150,6 +150,7 @@ def rounding_bounds(q, k, v, do, O, L, causal, scale):
       dV: sum_i P_ij |do_id| 2^-7
       dQ: scale sum_j (|dS_ij| 2^-7 + P_ij |dD_i|) |k_jd|
       dK: scale sum_i (|dS_ij| 2^-7 + P_ij |dD_i|) |q_id|.
+    Keys at or beyond a batch's kv_lens entry take no part (P_ij = 0).
     With keys of large norm along one direction these are not small against
     the gradients: dQ's component along it is a sum of large terms that
     cancel (sum_j dS_ij = 0 for every row), and the softmax of every row
@@ -159,9 +160,10 @@ def rounding_bounds(q, k, v, do, O, L, causal, scale):
     for b in range(B):
         for h in range(H):
             s = scale * (q[b, h] @ k[b, h].T)
-            if causal:
-                s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
-            P = np.exp(s - L[b, h][:, None])
+            keep = np.tril(np.ones((N, N), bool)) if causal else np.ones((N, N), bool)
+            if kv_lens is not None:
+                keep[:, int(kv_lens[b]):] = False
+            P = np.where(keep, np.exp(np.where(keep, s, 0.0) - np.where(np.isfinite(L[b, h]), L[b, h], 0.0)[:, None]), 0.0)
             dP = do[b, h] @ v[b, h].T
             D = (P * dP).sum(axis=1)
             dD = (np.abs(do[b, h]) * np.abs(O[b, h])).sum(axis=1) * 2.0 ** -7
