@@ -96,11 +96,15 @@ __global__ __launch_bounds__(256, (D == 256 || (D == 128 && !CAUSAL)) ? 1 : 2) v
     const int N = p.N;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = p.B * p.H * n_qblk;
-    const int w = xcd_remap(blockIdx.x, total);
-    const int bh = w / n_qblk;
-    int qb = w % n_qblk;
-    if (CAUSAL)
-        qb = n_qblk - 1 - qb;
+    int bh, qb;
+    if (CAUSAL) {
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, bh, qb);
+        qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
+    } else {
+        const int w = xcd_remap(blockIdx.x, total);
+        bh = w / n_qblk;
+        qb = w % n_qblk;
+    }
     const int b = bh / p.H;
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hf = lane >> 5;

@@ -49,9 +49,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     const int N = p.N;
     const int n_kb = (N + BKV - 1) / BKV;
     const int total = p.B * p.H * n_kb;
-    const int w = xcd_remap(blockIdx.x, total);
-    const int bh = w / n_kb;
-    const int kb = w % n_kb;               // causal: low key blocks have the most work
+    int bh, kb;
+    if (CAUSAL) {
+        causal_item(blockIdx.x, p.B * p.H, n_kb, bh, kb);   // low key blocks have the most work
+    } else {
+        const int w = xcd_remap(blockIdx.x, total);
+        bh = w / n_kb;
+        kb = w % n_kb;
+    }
     const int b = bh / p.H;
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hf = lane >> 5;

@@ -100,11 +100,15 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
     const int N = p.N;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = p.B * p.H * n_qblk;
-    const int w = xcd_remap(blockIdx.x, total);
-    const int bh = w / n_qblk;
-    int qb = w % n_qblk;
-    if (CAUSAL)
-        qb = n_qblk - 1 - qb;                // longest rows first
+    int bh, qb;
+    if (CAUSAL) {
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, bh, qb);
+        qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
+    } else {
+        const int w = xcd_remap(blockIdx.x, total);
+        bh = w / n_qblk;
+        qb = w % n_qblk;
+    }
     const int b = bh / p.H;
 
     const int tid = threadIdx.x;
@@ -367,11 +371,15 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p, float c_log2
     const int N = p.N;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = p.B * p.H * n_qblk;
-    const int w = xcd_remap(blockIdx.x, total);
-    const int bh = w / n_qblk;
-    int qb = w % n_qblk;
-    if (CAUSAL)
-        qb = n_qblk - 1 - qb;
+    int bh, qb;
+    if (CAUSAL) {
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, bh, qb);
+        qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
+    } else {
+        const int w = xcd_remap(blockIdx.x, total);
+        bh = w / n_qblk;
+        qb = w % n_qblk;
+    }
     const int b = bh / p.H;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;

@@ -116,4 +116,28 @@ __device__ __forceinline__ int xcd_remap(int bid, int total)
     return (bid % NXCD) * per_xcd + bid / NXCD;
 }
 
+// Work item of a causal grid of n_bh heads (b * H + h) times nblk row blocks
+// whose work falls with the block's rank: sets bh and rank, rank 0 being the
+// block with the most work.  Each XCD owns whole heads, as with xcd_remap,
+// but receives them interleaved in decreasing work: its r-th workgroup takes
+// rank r / hp of its head r % hp (hp heads per XCD), so the XCD runs
+// longest-first over all its heads.  In head-major order a later head's
+// longest blocks start after an earlier head's shortest ones and set the
+// finish time.  Head-major order remains when the heads do not split evenly
+// over the XCDs.
+__device__ __forceinline__ void causal_item(int bid, int n_bh, int nblk, int &bh, int &rank)
+{
+    constexpr int NXCD = 8;
+    if (n_bh % NXCD == 0) {
+        const int hp = n_bh / NXCD;
+        const int r = bid / NXCD;
+        bh = (bid % NXCD) * hp + r % hp;
+        rank = r / hp;
+    } else {
+        const int w = xcd_remap(bid, n_bh * nblk);
+        bh = w / nblk;
+        rank = w % nblk;
+    }
+}
+
 } // namespace fa
