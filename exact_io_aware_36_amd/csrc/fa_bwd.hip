@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, (D == 256 || (D == 128 && !CAUSAL)) ? 1 : 2) v
     const int total = p.B * p.H * n_qblk;
     int bh, qb;
     if (CAUSAL) {
-        causal_item(blockIdx.x, p.B * p.H, n_qblk, bh, qb);
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, qb);
         qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
     } else {
         const int w = xcd_remap(blockIdx.x, total);

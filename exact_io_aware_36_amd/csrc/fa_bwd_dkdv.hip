@@ -51,7 +51,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     const int total = p.B * p.H * n_kb;
     int bh, kb;
     if (CAUSAL) {
-        causal_item(blockIdx.x, p.B * p.H, n_kb, bh, kb);   // low key blocks have the most work
+        // low key blocks have the most work; Q and dO tiles are streamed
+        causal_item(blockIdx.x, p.B * p.H, n_kb, l2_group(N, 4 * D), bh, kb);
     } else {
         const int w = xcd_remap(blockIdx.x, total);
         bh = w / n_kb;

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
     const int total = p.B * p.H * n_qblk;
     int bh, qb;
     if (CAUSAL) {
-        causal_item(blockIdx.x, p.B * p.H, n_qblk, bh, qb);
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, qb);
         qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
     } else {
         const int w = xcd_remap(blockIdx.x, total);
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p, float c_log2
     const int total = p.B * p.H * n_qblk;
     int bh, qb;
     if (CAUSAL) {
-        causal_item(blockIdx.x, p.B * p.H, n_qblk, bh, qb);
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 8 * D), bh, qb);
         qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
     } else {
         const int w = xcd_remap(blockIdx.x, total);

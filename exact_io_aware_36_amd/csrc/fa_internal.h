@@ -119,25 +119,41 @@ __device__ __forceinline__ int xcd_remap(int bid, int total)
 // Work item of a causal grid of n_bh heads (b * H + h) times nblk row blocks
 // whose work falls with the block's rank: sets bh and rank, rank 0 being the
 // block with the most work.  Each XCD owns whole heads, as with xcd_remap,
-// but receives them interleaved in decreasing work: its r-th workgroup takes
-// rank r / hp of its head r % hp (hp heads per XCD), so the XCD runs
-// longest-first over all its heads.  In head-major order a later head's
-// longest blocks start after an earlier head's shortest ones and set the
-// finish time.  Head-major order remains when the heads do not split evenly
-// over the XCDs.
-__device__ __forceinline__ void causal_item(int bid, int n_bh, int nblk, int &bh, int &rank)
+// and takes them in groups of `group` heads; within a group the heads are
+// interleaved in decreasing work (its r-th item is rank r / gs of the group's
+// head r % gs), so the XCD runs longest-first across the group.  Head by head
+// (group = 1, xcd_remap's order) a later head's longest blocks start after an
+// earlier head's shortest ones and set the finish time; interleaving every
+// head of the XCD instead keeps all of their tiles in use at once, which
+// overflows the XCD's L2 and multiplies the L2 misses.  The group size is
+// chosen so the group's streamed tiles fit the L2 (l2_group).
+__device__ __forceinline__ void causal_item(int bid, int n_bh, int nblk, int group, int &bh,
+                                            int &rank)
 {
     constexpr int NXCD = 8;
     if (n_bh % NXCD == 0) {
-        const int hp = n_bh / NXCD;
-        const int r = bid / NXCD;
-        bh = (bid % NXCD) * hp + r % hp;
-        rank = r / hp;
+        const int hp = n_bh / NXCD;                  // heads per XCD
+        const int r = bid / NXCD;                    // dispatch rank within the XCD
+        const int g = min(max(group, 1), hp);
+        const int h0 = r / (g * nblk) * g;           // first head of r's group
+        const int gs = min(g, hp - h0);              // heads in that group
+        const int rr = r - h0 * nblk;
+        bh = (bid % NXCD) * hp + h0 + rr % gs;
+        rank = rr / gs;
     } else {
         const int w = xcd_remap(bid, n_bh * nblk);
         bh = w / nblk;
         rank = w % nblk;
     }
+}
+
+// Heads whose streamed [N][D] tensors (bytes_per_row bytes per row and head,
+// e.g. K and V in bf16: 4 D) fit one XCD's 4 MB L2 together; at least 1.
+__device__ __forceinline__ int l2_group(int N, int bytes_per_row)
+{
+    const unsigned long long per_head = (unsigned long long)N * (unsigned long long)bytes_per_row;
+    const unsigned long long g = (4ull << 20) / (per_head > 0 ? per_head : 1);
+    return g < 1 ? 1 : (g > 1024 ? 1024 : (int)g);
 }
 
 } // namespace fa
