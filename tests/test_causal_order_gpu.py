@@ -88,3 +88,37 @@ def test_causal_grid_order(fa, case):
         check_bf16(f"dQ[{bh}]", host(dq)[b, h, qr], sq)
         check_bf16(f"dK[{bh}]", host(dk)[b, h, kr], sk)
         check_bf16(f"dV[{bh}]", host(dv)[b, h, kr], sv)
+
+
+def test_causal_grid_order_fp8(fa):
+    """The FP8 forward's causal grid in groups of 2 heads with a last group of
+    1 (24 heads at N = 8192, d = 128): every output written, sampled rows of
+    every head within the quantisation bound of the FP8 parity tests."""
+    import oracle.fp8 as ofp8
+    from test_fp8_gpu import check_bound, oracle_inputs, qkv
+
+    B, H, N, d = 1, 24, 8192, 128
+    say(f"  causal order, fp8: B={B} H={H} N={N} d={d}")
+    inp = qkv(B, H, N, d, 6100)
+    q8, qs, k8, ks, v8, vs = oracle_inputs(inp, rot_seed=6101)
+    cuda = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    fa.fa_fwd_fp8(cuda(q8), cuda(k8), cuda(v8.transpose(0, 1, 3, 2)), cuda(qs), cuda(ks),
+                  cuda(vs.reshape(B, H)), o, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all(), "elements left unwritten"
+    o, lse = host(o), host(lse)
+    Q = ofp8.dequantize(q8, qs)
+    K = ofp8.dequantize(k8, ks)
+    V = ofp8.dequantize(v8, vs, 0)
+    rng = np.random.default_rng(6102)
+    for h in range(H):
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 6, replace=False)]))
+        Or, Lr = oracle.fwd_rows(Q[:, h:h + 1], K[:, h:h + 1], V[:, h:h + 1], rows, causal=True,
+                                 scale=scale)
+        bound = ofp8.p_quant_bound_rows(Q[0, h, rows], rows, K[0, h], V[0, h], Lr, causal=True,
+                                        scale=scale)
+        check_bound(f"O[h={h}]", o[0, h, rows], Or, bound)
+        check_lse(f"LSE[h={h}]", lse[0, h, rows], Lr)
