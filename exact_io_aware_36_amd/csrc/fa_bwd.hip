@@ -96,16 +96,9 @@ __global__ __launch_bounds__(256, (D == 256 || (D == 128 && !CAUSAL)) ? 1 : 2) v
     const int N = p.N;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = p.B * p.H * n_qblk;
-    __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
-    __shared__ int bcount;
     int bh, qb;
-    __shared__ int rsel;
-    if constexpr (SPARSE) {
-        int rank;
-        ranked_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, rank);
-        qb = mask_rank_select(p.mask, p.nb, false, rank, blist, &rsel);   // most nonzero blocks first
-    } else if (CAUSAL) {
-        ranked_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, qb);
+    if (CAUSAL) {
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, qb);
         qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
     } else {
         const int w = xcd_remap(blockIdx.x, total);
@@ -156,6 +149,8 @@ __global__ __launch_bounds__(256, (D == 256 || (D == 128 && !CAUSAL)) ? 1 : 2) v
     // the key tiles visited: dense, 0 .. up to the diagonal / key length;
     // block-sparse, the two tiles of every nonzero block of this query
     // block's mask row
+    __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
+    __shared__ int bcount;
     int n_tiles;
     if constexpr (SPARSE) {
         if (wave == 0)

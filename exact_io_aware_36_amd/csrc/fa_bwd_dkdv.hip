@@ -49,17 +49,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     const int N = p.N;
     const int n_kb = (N + BKV - 1) / BKV;
     const int total = p.B * p.H * n_kb;
-    __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
-    __shared__ int bcount;
     int bh, kb;
-    __shared__ int rsel;
-    if constexpr (SPARSE) {
-        int rank;
-        ranked_item(blockIdx.x, p.B * p.H, n_kb, l2_group(N, 4 * D), bh, rank);
-        kb = mask_rank_select(p.mask, p.nb, true, rank, blist, &rsel);    // most nonzero blocks first
-    } else if (CAUSAL) {
+    if (CAUSAL) {
         // low key blocks have the most work; Q and dO tiles are streamed
-        ranked_item(blockIdx.x, p.B * p.H, n_kb, l2_group(N, 4 * D), bh, kb);
+        causal_item(blockIdx.x, p.B * p.H, n_kb, l2_group(N, 4 * D), bh, kb);
     } else {
         const int w = xcd_remap(blockIdx.x, total);
         bh = w / n_kb;
@@ -111,6 +104,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     // the query tiles visited, in order: dense, all tiles from the diagonal
     // (causal) or from 0; block-sparse, the two tiles of every nonzero row
     // block of this key block's mask column
+    __shared__ int blist[SPARSE ? MAX_MASK_BLOCKS : 1];
+    __shared__ int bcount;
     const int n_qt = (N + BQ - 1) / BQ;
     const int qt_begin = (CAUSAL ? k0 / BQ : 0);
     int n_vis;

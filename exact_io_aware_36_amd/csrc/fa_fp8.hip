@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdArgs p)
     const int total = p.B * p.H * n_qblk;
     int bh, qb;
     if (CAUSAL) {
-        ranked_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 2 * D), bh, qb);
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 2 * D), bh, qb);
         qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
     } else {
         const int w = xcd_remap(blockIdx.x, total);

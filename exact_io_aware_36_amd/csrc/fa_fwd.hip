@@ -101,13 +101,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
     const int n_qblk = (N + BR - 1) / BR;
     const int total = p.B * p.H * n_qblk;
     int bh, qb;
-    __shared__ int rsel;
-    if constexpr (SPARSE) {
-        int rank;
-        ranked_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, rank);
-        qb = mask_rank_select(p.mask, p.nb, false, rank, blist, &rsel);   // most nonzero blocks first
-    } else if (CAUSAL) {
-        ranked_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, qb);
+    if (CAUSAL) {
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, qb);
         qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
     } else {
         const int w = xcd_remap(blockIdx.x, total);
@@ -378,7 +373,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p, float c_log2
     const int total = p.B * p.H * n_qblk;
     int bh, qb;
     if (CAUSAL) {
-        ranked_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 8 * D), bh, qb);
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 8 * D), bh, qb);
         qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
     } else {
         const int w = xcd_remap(blockIdx.x, total);

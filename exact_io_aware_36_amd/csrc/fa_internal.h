@@ -116,20 +116,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int total)
     return (bid % NXCD) * per_xcd + bid / NXCD;
 }
 
-// Work item of a grid of n_bh heads (b * H + h) times nblk row blocks whose
-// work falls with the block's rank (causal grids; block-sparse grids once
-// their rows are ranked by mask_rank_select): sets bh and rank, rank 0 being
-// the block with the most work.  Each XCD owns whole heads, as with
-// xcd_remap, and takes them in groups of `group` heads; within a group the
-// heads are interleaved in decreasing work (its r-th item is rank r / gs of
-// the group's head r % gs), so the XCD runs longest-first across the group.
-// Head by head (group = 1, xcd_remap's order) a later head's longest blocks
-// start after an earlier head's shortest ones and set the finish time;
-// interleaving every head of the XCD instead keeps all of their tiles in use
-// at once, which overflows the XCD's L2 and multiplies the L2 misses.  The
-// group size is chosen so the group's streamed tiles fit the L2 (l2_group);
-// heads of fewer than four blocks keep the head-major order.
-__device__ __forceinline__ void ranked_item(int bid, int n_bh, int nblk, int group, int &bh,
+// Work item of a causal grid of n_bh heads (b * H + h) times nblk row blocks
+// whose work falls with the block's rank: sets bh and rank, rank 0 being the
+// block with the most work.  Each XCD owns whole heads, as with xcd_remap,
+// and takes them in groups of `group` heads; within a group the heads are
+// interleaved in decreasing work (its r-th item is rank r / gs of the group's
+// head r % gs), so the XCD runs longest-first across the group.  Head by head
+// (group = 1, xcd_remap's order) a later head's longest blocks start after an
+// earlier head's shortest ones and set the finish time; interleaving every
+// head of the XCD instead keeps all of their tiles in use at once, which
+// overflows the XCD's L2 and multiplies the L2 misses.  The group size is
+// chosen so the group's streamed tiles fit the L2 (l2_group); heads of
+// fewer than four blocks keep the head-major order.
+__device__ __forceinline__ void causal_item(int bid, int n_bh, int nblk, int group, int &bh,
                                             int &rank)
 {
     constexpr int NXCD = 8;
@@ -150,43 +149,6 @@ __device__ __forceinline__ void ranked_item(int bid, int n_bh, int nblk, int gro
         bh = w / nblk;
         rank = w % nblk;
     }
-}
-
-// Block-sparse grids: the row (by_col: the column) of the nb x nb block mask
-// with the rank-th most nonzero blocks, ties to the lower index, so that
-// ranked_item hands out the rows with the most tiles first.  Every thread of
-// the workgroup calls it (it synchronises the workgroup twice); cnt is LDS
-// of at least nb ints, free again on return, sel one LDS int.  Above 64
-// blocks per side the rank itself is returned (the natural order): each
-// thread's nb serial mask reads and nb compares then cost more than the
-// balance gains (B1 H16 N16384 d128, 10 % of blocks: forward 0.234 ms in
-// natural order, 0.274 ranked; at N4096 d64, 25 %: 0.090 against 0.087).
-__device__ __forceinline__ int mask_rank_select(const uint8_t *mask, int nb, bool by_col, int rank,
-                                                int *cnt, int *sel)
-{
-    if (nb > 64)
-        return rank;
-    if (threadIdx.x == 0)
-        *sel = rank < nb ? rank : nb - 1;   // the ranks below are a permutation of 0 .. nb-1
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-        int c = 0;
-        for (int j = 0; j < nb; ++j)
-            c += (by_col ? mask[(size_t)j * nb + i] : mask[(size_t)i * nb + j]) != 0;
-        cnt[i] = c;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-        const int ci = cnt[i];
-        int r = 0;
-        for (int j = 0; j < nb; ++j) {
-            const int cj = cnt[j];
-            r += (cj > ci || (cj == ci && j < i)) ? 1 : 0;
-        }
-        if (r == rank)
-            *sel = i;
-    }
-    __syncthreads();
-    return __builtin_amdgcn_readfirstlane(*sel);
 }
 
 // Heads whose streamed [N][D] tensors (bytes_per_row bytes per row and head,
