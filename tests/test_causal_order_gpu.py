@@ -122,3 +122,28 @@ def test_causal_grid_order_fp8(fa):
                                         scale=scale)
         check_bound(f"O[h={h}]", o[0, h, rows], Or, bound)
         check_lse(f"LSE[h={h}]", lse[0, h, rows], Lr)
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if c[4] <= 128][:3] + [c for c in CASES if c[4] == 256],
+                         ids=lambda c: c[0])
+def test_causal_grid_order_other_tiles(fa, case):
+    """The forward's other key tiles (128 at d <= 128, 32 at d = 256) are
+    separate kernel instances taking the same work orders."""
+    label, B, H, N, d = case
+    tile = 32 if d == 256 else 128
+    say(f"  causal order, key tile {tile}: {label}: B={B} H={H} N={N} d={d}")
+    inp = workloads.random_qkv(B, H, N, d, seed=7000 + H * 7 + N + d)
+    q, k, v = (inp[n].contiguous().cuda() for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    o = nan_like(q)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=q.device)
+    fa.fa_fwd_ex(q, k, v, o, lse, causal=True, scale=scale, tile_n=tile)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all(), "elements left unwritten"
+    rng = np.random.default_rng(7001 + N + d)
+    rows = np.concatenate([bh * N + np.unique(np.concatenate([[0, N - 1], rng.choice(N, 4, replace=False)]))
+                           for bh in range(B * H)])
+    qf, kf, vf = (f64(inp[n]) for n in ("q", "k", "v"))
+    Or, Lr = oracle.fwd_rows(qf, kf, vf, rows, causal=True, scale=scale)
+    check_bf16("O[rows]", host(o).reshape(-1, d)[rows], Or)
+    check_lse("LSE[rows]", host(lse).reshape(-1)[rows], Lr)
