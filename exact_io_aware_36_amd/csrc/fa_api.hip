@@ -63,11 +63,18 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale, kv_lens, nullptr, 0};
     hipStream_t s = (hipStream_t)stream;
     if (dtype == FA_DTYPE_BF16) {
-        // key tiles: 64 or 128 at d = 64, 128; 32 or 64 at d = 256 (LDS)
+        // key tiles: 32, 64 or 128 at d = 64, 128; 32 or 64 at d = 256 (LDS)
         const bool ok = d == 256 ? (tile_n == 0 || tile_n == 32 || tile_n == 64)
-                                 : (tile_n == 0 || tile_n == 64 || tile_n == 128);
+                                 : (tile_n == 0 || tile_n == 32 || tile_n == 64 || tile_n == 128);
         if (!ok)
             return FA_ERR_UNSUPPORTED;
+        // default: the two-group kernel (32-key tiles) at d = 128 from
+        // N = 2048 on; below that, and at d = 64, the 64-key kernel measured
+        // faster (it has twice the workgroups, 128 query rows each)
+        if (tile_n == 0)
+            tile_n = (d == 128 && N >= 2048) ? 32 : 64;
+        if (d != 256 && tile_n == 32)
+            return from_hip(fa::launch_fwd_pp(a, d, causal != 0, s));
         return from_hip(fa::launch_fwd_bf16(a, d, tile_n, causal != 0, false, s));
     }
     if (dtype == FA_DTYPE_FP32) {

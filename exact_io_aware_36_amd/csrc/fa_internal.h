@@ -36,6 +36,8 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs &a, int d, int tile_n, bool causal, bool sparse,
                            hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal, hipStream_t s);
+// the two-group forward (fa_fwd_pp.hip): d = 64 or 128, 32-key tiles, dense
+hipError_t launch_fwd_pp(const FwdArgs &a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int d, bool causal, bool sparse, hipStream_t s);
 enum class BwdStage { Dot, DkDv, Dq };
 // the dK, dV launch(es) of the backward (fa_bwd_dkdv.hip)

@@ -97,10 +97,12 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  * fa_fwd with an explicit key/value tile length tile_n (the B_c of the
  * pages' block-size constraint B_r*d + 2*B_c*d <= M, "FlashAttention:
  * Mathematical Foundations ...", section "IO-Aware Tiling Algorithm").
- * tile_n = 0 picks the default (64 for bf16, 32 for fp32); 64 and 128 are
- * built for bf16 at d = 64 and 128, 32 and 64 for bf16 at d = 256 (two
- * stages of 128-key tiles would not fit in LDS), and 32 for fp32.  Other
- * values give FA_ERR_UNSUPPORTED.
+ * tile_n = 0 picks the default: for bf16 at d = 128 and N >= 2048 the
+ * 32-key kernel, otherwise 64 (bf16) or 32 (fp32).  Built: for bf16 at
+ * d = 64 and 128, 32 (a workgroup of 256 query rows in two wave groups that
+ * alternate between matrix products and the softmax), 64 and 128 (128 query
+ * rows); at d = 256, 32 and 64 (two stages of 128-key tiles would not fit in
+ * LDS); 32 for fp32.  Other values give FA_ERR_UNSUPPORTED.
  * Results equal fa_fwd's up to rounding order.
  */
 fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,

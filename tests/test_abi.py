@@ -93,10 +93,10 @@ def test_fwd_rejects(lib, kw, want):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(tile=32), UNSUPPORTED), (dict(tile=256), UNSUPPORTED), (dict(tile=-1), UNSUPPORTED),
+    (dict(tile=48), UNSUPPORTED), (dict(tile=512), UNSUPPORTED), (dict(tile=-1), UNSUPPORTED),
     (dict(tile=64, dtype=FP32), UNSUPPORTED), (dict(tile=16, dtype=FP32), UNSUPPORTED),
     (dict(tile=64, d=80), UNSUPPORTED), (dict(tile=64, q=None), INVALID),
-    (dict(tile=128, d=256), UNSUPPORTED), (dict(tile=32, d=128), UNSUPPORTED),
+    (dict(tile=128, d=256), UNSUPPORTED), (dict(tile=16, d=128), UNSUPPORTED),
 ])
 def test_fwd_ex_rejects(lib, kw, want):
     assert fwd(lib, **kw) == want

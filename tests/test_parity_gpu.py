@@ -112,7 +112,7 @@ SMALL = [
 @pytest.mark.parametrize("shape", SMALL)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("padded", [False, True])
-@pytest.mark.parametrize("tile_n", [64, 128])
+@pytest.mark.parametrize("tile_n", [32, 64, 128])
 def test_fwd_small(fa, shape, causal, padded, tile_n):
     B, H, N, d = shape
     say(f"  fwd bf16 B={B} H={H} N={N} d={d} causal={causal} padded={padded} tile={tile_n}")
@@ -345,7 +345,7 @@ def test_workload_long_context_causal(fa):
         check_bf16(f"dV[h={h}]", host(dv)[0, h, kr], sv)
 
 
-@pytest.mark.parametrize("tile_n", [64, 128])
+@pytest.mark.parametrize("tile_n", [32, 64, 128])
 def test_workload_long_context_tiles(fa, tile_n):
     """The key-tile sweep: every tile length gives the same forward."""
     w = workloads.WORKLOADS["long_context_causal"]
