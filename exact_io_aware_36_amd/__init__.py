@@ -15,6 +15,7 @@ built, and every call raises FAError on a non-zero status.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -344,44 +345,61 @@ def fa_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, o, lse, causal=Fals
 
 
 # -- the same calls with torch-allocated outputs ------------------------------
+#
+# Outputs and workspaces are allocated on the stream the kernels run on, so
+# that torch's caching allocator does not hand a workspace freed on return to
+# another stream's allocation while the kernels still use it.
+
+def _on_stream(t: torch.Tensor, stream):
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, torch.cuda.Stream):
+        return torch.cuda.stream(stream)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.stream(torch.cuda.ExternalStream(s, device=t.device))
+
 
 def fwd(q, k, v, causal=False, scale=None, kv_lens=None, tile_n=0, stream=None):
     """Return (O, LSE)."""
     B, H, N, d = _shape(q)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd_ex(q, k, v, o, lse, causal=causal, scale=scale, kv_lens=kv_lens, tile_n=tile_n,
-              stream=stream)
+    with _on_stream(q, stream):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        fa_fwd_ex(q, k, v, o, lse, causal=causal, scale=scale, kv_lens=kv_lens, tile_n=tile_n,
+                  stream=stream)
     return o, lse
 
 
 def bwd(q, k, v, o, dout, lse, causal=False, scale=None, kv_lens=None, stream=None):
     """Return (dQ, dK, dV)."""
     B, H, N, d = _shape(q)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
-    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal=causal, scale=scale, kv_lens=kv_lens,
-           stream=stream)
+    with _on_stream(q, stream):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+        fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal=causal, scale=scale, kv_lens=kv_lens,
+               stream=stream)
     return dq, dk, dv
 
 
 def bwd_blocksparse(q, k, v, o, dout, lse, block_mask, mask_block=128, scale=None, stream=None):
     """Return (dQ, dK, dV) of the block-sparse forward."""
     B, H, N, d = _shape(q)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
-    fa_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, ws, block_mask, mask_block=mask_block,
-                       scale=scale, stream=stream)
+    with _on_stream(q, stream):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+        fa_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, ws, block_mask,
+                           mask_block=mask_block, scale=scale, stream=stream)
     return dq, dk, dv
 
 
 def fwd_blocksparse(q, k, v, block_mask, mask_block=128, scale=None, stream=None):
     """Return (O, LSE)."""
     B, H, N, d = _shape(q)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_block=mask_block, scale=scale,
-                       stream=stream)
+    with _on_stream(q, stream):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        fa_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_block=mask_block, scale=scale,
+                           stream=stream)
     return o, lse
 
 
@@ -390,12 +408,13 @@ def fwd_splitkv(q, k, v, causal=False, scale=None, kv_lens=None, num_splits=0, s
     [B, H, Nk, d]; return (O [B, H, Nq, d], LSE [B, H, Nq])."""
     B, H, Nq, d = _shape(q)
     Nk = int(k.shape[2]) if k.dim() == 4 else 0
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    nbytes = fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
-    fa_fwd_splitkv(q, k, v, o, lse, ws, causal=causal, scale=scale, kv_lens=kv_lens,
-                   num_splits=num_splits, stream=stream)
+    with _on_stream(q, stream):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        nbytes = fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+        fa_fwd_splitkv(q, k, v, o, lse, ws, causal=causal, scale=scale, kv_lens=kv_lens,
+                       num_splits=num_splits, stream=stream)
     return o, lse
 
 
@@ -403,9 +422,10 @@ def merge(o_parts, lse_parts, out_dtype=torch.bfloat16, stream=None):
     """Combine partial results o_parts [S, R, d], lse_parts [S, R]; return
     (O [R, d] in out_dtype, LSE [R])."""
     S, R, d = (int(x) for x in o_parts.shape)
-    o = torch.empty((R, d), dtype=out_dtype, device=o_parts.device)
-    lse = torch.empty((R,), dtype=torch.float32, device=o_parts.device)
-    fa_merge(o_parts, lse_parts, o, lse, stream=stream)
+    with _on_stream(o_parts, stream):
+        o = torch.empty((R, d), dtype=out_dtype, device=o_parts.device)
+        lse = torch.empty((R,), dtype=torch.float32, device=o_parts.device)
+        fa_merge(o_parts, lse_parts, o, lse, stream=stream)
     return o, lse
 
 
@@ -413,13 +433,15 @@ def quantize_fp8(x, block_rows=128, signs=None, transpose=False, stream=None):
     """Return (codes uint8, descale fp32) of bf16 x [B, H, N, d]."""
     B, H, N, d = _shape(x)
     shape = (B, H, d, N) if transpose else (B, H, N, d)
-    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
-    nblk = (N + 127) // 128 if block_rows else 1
-    descale = torch.empty((B, H, nblk) if block_rows else (B, H), dtype=torch.float32, device=x.device)
-    nbytes = fa_quantize_fp8_workspace_bytes(B, H, N, d, block_rows)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
-    fa_quantize_fp8(x, x8, descale, block_rows=block_rows, signs=signs, transpose=transpose,
-                    workspace=ws, stream=stream)
+    with _on_stream(x, stream):
+        x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
+        nblk = (N + 127) // 128 if block_rows else 1
+        descale = torch.empty((B, H, nblk) if block_rows else (B, H), dtype=torch.float32,
+                              device=x.device)
+        nbytes = fa_quantize_fp8_workspace_bytes(B, H, N, d, block_rows)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+        fa_quantize_fp8(x, x8, descale, block_rows=block_rows, signs=signs, transpose=transpose,
+                        workspace=ws, stream=stream)
     return x8, descale
 
 
@@ -443,19 +465,21 @@ def fa_fwd_kvouter(q, k, v, o, lse, workspace, causal=False, scale=None, stream=
 def fwd_kvouter(q, k, v, causal=False, scale=None, stream=None):
     """Key/value-outer forward with its own workspace; return (O, LSE)."""
     B, H, N, d = _shape(q)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     nbytes = fa_fwd_kvouter_workspace_bytes(B, H, N, d)
     _require(nbytes > 0, "unsupported size for the key/value-outer forward")
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    fa_fwd_kvouter(q, k, v, o, lse, ws, causal=causal, scale=scale, stream=stream)
+    with _on_stream(q, stream):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        fa_fwd_kvouter(q, k, v, o, lse, ws, causal=causal, scale=scale, stream=stream)
     return o, lse
 def fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, causal=False, scale=None, kv_lens=None,
             stream=None):
     """FP8 forward on quantised inputs; return (O bf16 [B, H, N, d], LSE)."""
     B, H, N, d = (int(x) for x in q8.shape)
-    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    fa_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, o, lse, causal=causal, scale=scale,
-               kv_lens=kv_lens, stream=stream)
+    with _on_stream(q8, stream):
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+        fa_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, o, lse, causal=causal,
+                   scale=scale, kv_lens=kv_lens, stream=stream)
     return o, lse
