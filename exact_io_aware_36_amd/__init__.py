@@ -24,6 +24,7 @@ import torch  # loads torch's HIP runtime first, so libfa.so binds to the same o
 
 __all__ = [
     "FAError", "fa_status_str", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_bytes",
+    "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows",
     "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
     "fwd", "bwd", "fwd_blocksparse", "bwd_blocksparse", "library_path",
 ]
@@ -69,6 +70,11 @@ _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
 _lib.fa_bwd.restype = _i
 _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                         _vp, _i, _vp, _sz, _vp]
+_lib.fa_bwd_noalloc.restype = _i
+_lib.fa_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                _f, _vp, _i, _vp]
+_lib.fa_bwd_noalloc_max_rows.restype = _i
+_lib.fa_bwd_noalloc_max_rows.argtypes = []
 _lib.fa_bwd_preprocess.restype = _i
 _lib.fa_bwd_preprocess.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]
 _lib.fa_bwd_dkdv.restype = _i
@@ -202,6 +208,24 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal=False, scale=Non
                      _ptr(dv), B, H, N, d, int(bool(causal)), _scale(scale, d), _ptr(kv_lens),
                      _dtype(q), _ptr(workspace), ws_bytes, _stream(q, stream))
     _check_rc(rc, "fa_bwd")
+
+
+def fa_bwd_noalloc_max_rows() -> int:
+    return int(_lib.fa_bwd_noalloc_max_rows())
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal=False, scale=None, kv_lens=None,
+                   stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, o, dout, dq, dk, dv)
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * N,
+             "lse must be contiguous fp32 [B, H, N]")
+    if kv_lens is not None:
+        _require(kv_lens.dtype == torch.int32 and kv_lens.numel() == B, "kv_lens must be int32 [B]")
+    rc = _lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                             _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), _scale(scale, d),
+                             _ptr(kv_lens), _dtype(q), _stream(q, stream))
+    _check_rc(rc, "fa_bwd_noalloc")
 
 
 def _ws_bytes(workspace):

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_internal.h"
 #include "fa_kvouter.h"
@@ -139,6 +141,77 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
     float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
     fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, ws, ws2, B, H, N, scale, kv_lens};
     return from_hip(fa::launch_bwd_bf16(a, d, causal != 0, false, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// The backward without caller workspace.  Its scratch (D, then LSE * log2(e),
+// fp32, one value per query row each) lives in this file-scope device array:
+// every GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` only names the symbol; its device address comes
+// from hipGetSymbolAddress, once per device, kept in scratch_ptr[].
+constexpr int kNoAllocMaxRows = 1 << 20;     // B * H * N limit: 8 MiB of scratch
+static __device__ __align__(256) float scratch[2 * kNoAllocMaxRows];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float *scratch_ptr[kMaxDevices];
+
+// device address of `scratch` on the current device (looked up on the
+// device's first call)
+hipError_t scratch_on_current_device(float **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        scratch_ptr[dev] = (float *)p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+} // namespace
+
+int fa_bwd_noalloc_max_rows(void) { return kNoAllocMaxRows; }
+
+fa_status fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                         const void *dout, const float *lse, void *dq, void *dk, void *dv, int B,
+                         int H, int N, int d, int causal, float scale, const int32_t *kv_lens,
+                         fa_dtype dtype, fa_stream_t stream)
+{
+    // the argument checks of fa_bwd, with a stand-in workspace of the size
+    // it requires (none is read)
+    const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+    fa_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, kv_lens, dtype,
+                             (const void *)256, need);
+    if (st != FA_OK)
+        return st;
+    if ((int64_t)B * H * N > kNoAllocMaxRows)
+        return FA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    if (s) {   // the stream must belong to the current device, whose scratch is used
+        int cur = -1, sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(s, &sdev) != hipSuccess)
+            return FA_ERR_LAUNCH;
+        if (cur != sdev)
+            return FA_ERR_INVALID_ARG;
+    }
+    float *ws = nullptr;
+    if (scratch_on_current_device(&ws) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    // D in the first half, LSE * log2(e) in the second; every row the kernels
+    // read is written by the preprocessing kernel first, so nothing is cleared
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, ws, ws + kNoAllocMaxRows, B, H, N, scale,
+                  kv_lens};
+    return from_hip(fa::launch_bwd_bf16(a, d, causal != 0, false, s));
 }
 
 fa_status fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, int H,

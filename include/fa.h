@@ -141,6 +141,32 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
                  size_t workspace_bytes, fa_stream_t stream);
 
 /*
+ * fa_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results, with the backward's scratch (the D and
+ * LSE*log2(e) row vectors) in a fixed device array inside the library
+ * instead of a caller workspace.  It allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library call.
+ *   Arguments as fa_bwd, without workspace.  stream must be NULL or a stream
+ *   of the current device (whose copy of the array is used).
+ *   Limit: B*H*N <= fa_bwd_noalloc_max_rows() (2^20 rows, 8 MiB of scratch
+ *   per GPU, held until the process ends); larger sizes give
+ *   FA_ERR_WORKSPACE.  A stream of another device gives FA_ERR_INVALID_ARG.
+ *   Other errors as fa_bwd.
+ * All calls on one GPU share its array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and give undefined results; calls
+ * ordered on one stream are safe.  Nothing in the array needs clearing
+ * between calls (every value read is written first by the same call).
+ */
+fa_status fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                         const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                         int B, int H, int N, int d, int causal, float scale,
+                         const int32_t *kv_lens, fa_dtype dtype, fa_stream_t stream);
+
+/* The row limit B*H*N of fa_bwd_noalloc. */
+int fa_bwd_noalloc_max_rows(void);
+
+/*
  * The three launches fa_bwd makes, callable one by one on the same stream
  * and in this order (results equal fa_bwd's bit for bit).  Useful to time
  * or overlap the stages separately.  Arguments mean what they mean for

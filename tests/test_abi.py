@@ -298,3 +298,24 @@ def kvouter(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, sca
 ])
 def test_kvouter_rejects(lib, kw, want):
     assert kvouter(lib, **kw) == want
+
+
+def noalloc(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=2, N=256, d=64,
+            causal=0, scale=0.125, lens=None, dtype=BF16):
+    return lib.fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, causal, scale, lens,
+                              dtype, None)
+
+
+def test_bwd_noalloc_limit(lib):
+    assert lib.fa_bwd_noalloc_max_rows() == 1 << 20
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=(1 << 20) + 1, H=1), WORKSPACE), (dict(B=2, H=8, N=65537), WORKSPACE),
+    (dict(q=None), INVALID), (dict(dq=None), INVALID), (dict(N=0), INVALID),
+    (dict(scale=0.0), INVALID), (dict(d=80), UNSUPPORTED), (dict(dtype=FP32), UNSUPPORTED),
+    (dict(dk=MIS), INVALID),
+])
+def test_bwd_noalloc_rejects(lib, kw, want):
+    assert noalloc(lib, **kw) == want
+
