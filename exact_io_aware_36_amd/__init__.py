@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/fa.h.  The functions named like
-the C entry points (fa_fwd, fa_fwd_ex, fa_bwd, fa_bwd_workspace_bytes,
+the C entry points (fa_fwd, fa_fwd_ex, fa_bwd, fa_bwd_ex, fa_bwd_workspace_bytes,
 fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_fwd_blocksparse, fa_bwd_blocksparse,
 fa_status_str)
 take torch device tensors, read their shapes and pointers and call the C
@@ -24,7 +24,7 @@ import torch  # loads torch's HIP runtime first, so libfa.so binds to the same o
 
 __all__ = [
     "FAError", "fa_status_str", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_bytes",
-    "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows",
+    "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows",
     "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
     "fwd", "bwd", "fwd_blocksparse", "bwd_blocksparse", "library_path",
 ]
@@ -70,6 +70,9 @@ _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
 _lib.fa_bwd.restype = _i
 _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                         _vp, _i, _vp, _sz, _vp]
+_lib.fa_bwd_ex.restype = _i
+_lib.fa_bwd_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                           _vp, _i, _i, _vp, _sz, _vp]
 _lib.fa_bwd_noalloc.restype = _i
 _lib.fa_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                 _f, _vp, _i, _vp]
@@ -208,6 +211,21 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal=False, scale=Non
                      _ptr(dv), B, H, N, d, int(bool(causal)), _scale(scale, d), _ptr(kv_lens),
                      _dtype(q), _ptr(workspace), ws_bytes, _stream(q, stream))
     _check_rc(rc, "fa_bwd")
+
+
+def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal=False, scale=None,
+              kv_lens=None, tile_n=0, stream=None):
+    B, H, N, d = _shape(q)
+    _same(q, k, v, o, dout, dq, dk, dv)
+    _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * N,
+             "lse must be contiguous fp32 [B, H, N]")
+    if kv_lens is not None:
+        _require(kv_lens.dtype == torch.int32 and kv_lens.numel() == B, "kv_lens must be int32 [B]")
+    rc = _lib.fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), _scale(scale, d),
+                        _ptr(kv_lens), _dtype(q), int(tile_n), _ptr(workspace),
+                        _ws_bytes(workspace), _stream(q, stream))
+    _check_rc(rc, "fa_bwd_ex")
 
 
 def fa_bwd_noalloc_max_rows() -> int:
@@ -394,14 +412,14 @@ def fwd(q, k, v, causal=False, scale=None, kv_lens=None, tile_n=0, stream=None):
     return o, lse
 
 
-def bwd(q, k, v, o, dout, lse, causal=False, scale=None, kv_lens=None, stream=None):
+def bwd(q, k, v, o, dout, lse, causal=False, scale=None, kv_lens=None, tile_n=0, stream=None):
     """Return (dQ, dK, dV)."""
     B, H, N, d = _shape(q)
     with _on_stream(q, stream):
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         ws = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
-        fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal=causal, scale=scale, kv_lens=kv_lens,
-               stream=stream)
+        fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, ws, causal=causal, scale=scale,
+                  kv_lens=kv_lens, tile_n=tile_n, stream=stream)
     return dq, dk, dv
 
 

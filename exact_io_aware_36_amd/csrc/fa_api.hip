@@ -65,9 +65,10 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale, kv_lens, nullptr, 0};
     hipStream_t s = (hipStream_t)stream;
     if (dtype == FA_DTYPE_BF16) {
-        // key tiles: 32, 64 or 128 at d = 64, 128; 32 or 64 at d = 256 (LDS)
+        // key tiles: 32, 64, 128 or 256 at d = 64, 128; 32 or 64 at d = 256 (LDS)
         const bool ok = d == 256 ? (tile_n == 0 || tile_n == 32 || tile_n == 64)
-                                 : (tile_n == 0 || tile_n == 32 || tile_n == 64 || tile_n == 128);
+                                 : (tile_n == 0 || tile_n == 32 || tile_n == 64 || tile_n == 128 ||
+                                    tile_n == 256);
         if (!ok)
             return FA_ERR_UNSUPPORTED;
         // default: the two-group kernel (32-key tiles) at d = 128 from
@@ -126,6 +127,25 @@ static fa_status check_bwd(const void *q, const void *k, const void *v, const vo
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return FA_ERR_WORKSPACE;
     return FA_OK;
+}
+
+fa_status fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                    const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+                    int causal, float scale, const int32_t *kv_lens, fa_dtype dtype, int tile_n,
+                    void *workspace, size_t workspace_bytes, fa_stream_t stream)
+{
+    fa_status st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, kv_lens, dtype,
+                             workspace, workspace_bytes);
+    if (st != FA_OK)
+        return st;
+    // query rows per tile of the dK/dV kernel: 64, or 128 at d <= 128
+    if (!(tile_n == 0 || tile_n == 64 || (tile_n == 128 && d != 256)))
+        return FA_ERR_UNSUPPORTED;
+    float *ws = (float *)workspace;
+    float *ws2 = (float *)((char *)workspace + ws_region(B, H, N));
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, ws, ws2, B, H, N, scale, kv_lens};
+    a.tile_q = tile_n;
+    return from_hip(fa::launch_bwd_bf16(a, d, causal != 0, false, (hipStream_t)stream));
 }
 
 fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,

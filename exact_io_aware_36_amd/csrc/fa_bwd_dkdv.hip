@@ -27,11 +27,12 @@ namespace {
 // two accumulators of a wave's 32 keys do not fit one wave's registers, so
 // the work is split over two launches: MODE 1 (dV only: S, P, dV^T += dO^T P)
 // and MODE 2 (dK only: S, dP, dS, dK^T += Q^T dS), recomputing S once more.
-template <int D, bool CAUSAL, bool SPARSE, int MODE>
+template <int D, int BQ, bool CAUSAL, bool SPARSE, int MODE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs p, float c_log2)
 {
     constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
-    constexpr int BKV = 128, BQ = 64;
+    constexpr int BKV = 128;
+    static_assert(BQ == 64 || BQ == 128, "query tile");
     constexpr int KSTEPS = D / 16;
     constexpr int NQC = BQ / 32;           // 32-query chunks per tile
     constexpr int NDB = D / 32;
@@ -131,15 +132,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         const int qbase = it * BQ;
         dma.issue(qrs, qbase, qd, wave);
         dma.issue(grs, qbase, gd, wave);
-        if (wave == 0)
-            buffer_to_lds4(lrs, ld, lane * 4, qbase * 4);
-        else if (wave == 1 && DO_DK)
-            buffer_to_lds4(drs, dd, lane * 4, qbase * 4);
+        // 64 rows of LSE (even waves) and of D (odd waves) per instruction
+        const int part = wave >> 1;
+        if (part < BQ / 64) {
+            if ((wave & 1) == 0)
+                buffer_to_lds4(lrs, ld + part * 64, lane * 4, (qbase + part * 64) * 4);
+            else if (DO_DK)
+                buffer_to_lds4(drs, dd + part * 64, lane * 4, (qbase + part * 64) * 4);
+        }
     };
 
-    // MASKED applies the causal mask.  Only the two query tiles that hold this
-    // workgroup's diagonal (the first two visited, qbase = k0 and k0 + 64)
-    // need it; they are peeled off the main loop below.  Key padding needs no
+    // MASKED applies the causal mask.  Only the query tiles that hold this
+    // workgroup's diagonal (the first visited: qbase = k0 and, with 64-row
+    // tiles, k0 + 64) need it; the first step is peeled off the main loop
+    // below.  Key padding needs no
     // mask here: a padded key's P reaches only its own dK, dV row, which the
     // store writes as zero.
     auto compute = [&](auto masked, int it, const bf16 *qt, const bf16 *gt, const float *lt,
@@ -288,26 +294,34 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     }
 }
 
-template <int D, bool CAUSAL, bool SPARSE, int MODE>
+template <int D, int BQ, bool CAUSAL, bool SPARSE, int MODE>
 hipError_t launch_dkdv_mode(const BwdArgs &a, hipStream_t s)
 {
     BwdArgs args = a;
     float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     const int n_kb = (a.N + 127) / 128;
-    return hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, CAUSAL, SPARSE, MODE>,
+    return hipLaunchKernel((const void *)&bwd_dkdv_kernel<D, BQ, CAUSAL, SPARSE, MODE>,
                            dim3(a.B * a.H * n_kb), dim3(256), kargs, 0, s);
 }
 
-// d = 64, 128: one launch for dK and dV; d = 256: a dV launch and a dK launch
+// d = 64, 128: one launch for dK and dV; d = 256: a dV launch and a dK launch.
+// Query tiles of 64 rows, or 128 at d <= 128 (two stages of 128-row Q and
+// dO tiles at d = 256 would need 256 KB of LDS).
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_dkdv(const BwdArgs &a, hipStream_t s)
 {
     if constexpr (D == 256) {
-        hipError_t e = launch_dkdv_mode<D, CAUSAL, SPARSE, 1>(a, s);
-        return e == hipSuccess ? launch_dkdv_mode<D, CAUSAL, SPARSE, 2>(a, s) : e;
+        if (a.tile_q != 0 && a.tile_q != 64)
+            return hipErrorInvalidValue;
+        hipError_t e = launch_dkdv_mode<D, 64, CAUSAL, SPARSE, 1>(a, s);
+        return e == hipSuccess ? launch_dkdv_mode<D, 64, CAUSAL, SPARSE, 2>(a, s) : e;
     } else {
-        return launch_dkdv_mode<D, CAUSAL, SPARSE, 0>(a, s);
+        if (a.tile_q == 128)
+            return launch_dkdv_mode<D, 128, CAUSAL, SPARSE, 0>(a, s);
+        if (a.tile_q != 0 && a.tile_q != 64)
+            return hipErrorInvalidValue;
+        return launch_dkdv_mode<D, 64, CAUSAL, SPARSE, 0>(a, s);
     }
 }
 

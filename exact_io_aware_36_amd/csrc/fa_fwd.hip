@@ -479,6 +479,165 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p, float c_log2
 }
 
 // ---------------------------------------------------------------------------
+// bf16 forward with 256-key tiles: the block-size end of the key-tile sweep
+// (the pages report fewer HBM accesses and less run time for larger blocks
+// up to about 256, "Attention" chapter of learn-kernels.com, paragraph on
+// the block-size sweep).  One LDS stage holds the whole K and V tile (128 KB
+// at d = 128, 64 KB at d = 64), so one workgroup of 4 waves runs per CU and
+// a tile's copy cannot overlap the previous tile's work: copy, barrier, the
+// tile's eight 32-key chunks (S, masks, softmax, P V each, as in
+// fwd_bf16_kernel), barrier.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_bf16_t256_kernel(FwdArgs p, float c_log2)
+{
+    constexpr int BR = 128, BC = 256;
+    constexpr int KSTEPS = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int NCH = BC / 32;            // 32-key chunks per tile
+
+    __shared__ __attribute__((aligned(1024))) bf16 ks[BC * D];
+    __shared__ __attribute__((aligned(1024))) bf16 vs[BC * D];
+
+    const int N = p.N;
+    const int n_qblk = (N + BR - 1) / BR;
+    const int total = p.B * p.H * n_qblk;
+    int bh, qb;
+    if (CAUSAL) {
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, qb);
+        qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
+    } else {
+        const int w = xcd_remap(blockIdx.x, total);
+        bh = w / n_qblk;
+        qb = w % n_qblk;
+    }
+    const int b = bh / p.H;
+    const int tid = threadIdx.x;
+    const int wave = wave_id(), lane = tid & 63;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int q0 = qb * BR;
+    const int wq0 = q0 + wave * 32;
+    const int qrow = wq0 + l32;
+
+    const size_t head_off = (size_t)bh * N * D;
+    const bf16 *Q = (const bf16 *)p.q + head_off;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc((const bf16 *)p.k + head_off, N, D);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc((const bf16 *)p.v + head_off, N, D);
+
+    int kv_len = N;
+    if (p.kv_lens) {
+        kv_len = p.kv_lens[b];
+        kv_len = kv_len < 0 ? 0 : (kv_len > N ? N : kv_len);
+    }
+    int kv_end = kv_len;
+    if (CAUSAL)
+        kv_end = min(kv_end, q0 + BR);
+    const int n_tiles = (kv_end + BC - 1) / BC;
+
+    bf16x8 qreg[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+        qreg[s] = qrow < N ? *(const bf16x8 *)(Q + (size_t)qrow * D + s * 16 + hf * 8) : bf16x8{};
+
+    using Dma = TileDma<BC, D, 4>;
+    Dma dma;
+    dma.init(wave);
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        oacc[db] = f32x16{};
+
+    for (int t = 0; t < n_tiles; ++t) {
+        dma.issue(krs, t * BC, ks, wave);
+        dma.issue(vrs, t * BC, vs, wave);
+        wait_vmem();
+        __syncthreads();
+        for (int c = 0; c < NCH; ++c) {
+            const int kbase = t * BC + c * 32;
+            if (kbase >= kv_end || (CAUSAL && kbase > wq0 + 31))
+                break;                       // chunks only grow from here (wave-uniform)
+            f32x16 s = f32x16{};
+            bf16x8 ka[KSTEPS];
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st)
+                ka[st] = ld_row8<D>(ks, c * 32 + l32, st * 16 + hf * 8);
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st)
+                s = mfma_bf16(ka[st], qreg[st], s);
+            if (kbase + 32 > kv_len || (CAUSAL && kbase + 31 > wq0)) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kbase + 8 * (i / 4) + 4 * hf + (i % 4);
+                    if (key >= kv_len || (CAUSAL && key > qrow))
+                        s[i] = -INFINITY;
+                }
+            }
+            // running maximum moved lazily (threshold TAU), as in fwd_bf16_kernel
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                mx = fmaxf(mx, s[i]);
+            const float mt = pair_max(mx) * c_log2;
+            if (__any(mt > m + TAU)) {
+                const float m_new = fmaxf(m, mt);
+                const float alpha = exp2_hw(m - m_new);
+                m = m_new;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] *= alpha;
+            }
+            const float m_use = (m == -INFINITY) ? 0.f : m;
+            bf16x8 pb[2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv = exp2_hw(fmaf(s[i], c_log2, -m_use));
+                lsum += pv;
+                pb[i / 8][i % 8] = (bf16)pv;
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const bf16x8 v0 = ld_tr8<D>(vs, c * 32, db * 32);
+                const bf16x8 v1 = ld_tr8<D>(vs, c * 32 + 16, db * 32);
+                oacc[db] = mfma_bf16(v0, pb[0], oacc[db]);
+                oacc[db] = mfma_bf16(v1, pb[1], oacc[db]);
+            }
+        }
+        __syncthreads();                     // every wave done with this tile
+    }
+
+    const float ltot = pair_sum(lsum);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (qrow < N) {
+        bf16 *O = (bf16 *)p.o + head_off + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ov[e] = (bf16)(oacc[db][4 * g + e] * inv);
+                *(bf16x4 *)(O + db * 32 + 8 * g + 4 * hf) = ov;
+            }
+        if (hf == 0)
+            p.lse[(size_t)bh * N + qrow] = ltot > 0.f ? kLn2 * (m + __log2f(ltot)) : -INFINITY;
+    }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_t256_inst(const FwdArgs &a, hipStream_t s)
+{
+    const int n_qblk = (a.N + 127) / 128;
+    FwdArgs args = a;
+    float c = a.scale * kLog2e;
+    void *kargs[] = {&args, &c};
+    return hipLaunchKernel((const void *)&fwd_bf16_t256_kernel<D, CAUSAL>, dim3(a.B * a.H * n_qblk),
+                           dim3(256), kargs, 0, s);
+}
+
+// ---------------------------------------------------------------------------
 template <int D, int BC, bool CAUSAL, bool SPARSE>
 static hipError_t launch_bf16_inst(const FwdArgs &a, hipStream_t s)
 {
@@ -515,6 +674,11 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, int tile_n, bool causal, boo
         return launch_bf16_d_bc<128, 128>(a, causal, sparse, s);
     if (d == 256 && tile_n == 64)
         return launch_bf16_d_bc<256, 64>(a, causal, sparse, s);
+    if (tile_n == 256 && !sparse && (d == 64 || d == 128)) {
+        if (d == 64)
+            return causal ? launch_t256_inst<64, true>(a, s) : launch_t256_inst<64, false>(a, s);
+        return causal ? launch_t256_inst<128, true>(a, s) : launch_t256_inst<128, false>(a, s);
+    }
     if (d == 256 && tile_n == 32)
         return launch_bf16_d_bc<256, 32>(a, causal, sparse, s);
     return hipErrorInvalidValue;

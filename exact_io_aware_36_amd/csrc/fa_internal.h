@@ -30,6 +30,7 @@ struct BwdArgs {
     const int32_t *kv_lens;
     const uint8_t *mask;    // block mask (sparse launches only)
     int nb;                 // mask blocks per side (sparse launches only)
+    int tile_q = 0;         // query rows per tile of the dK/dV kernel (0 = 64; 64 or 128)
 };
 
 // Kernel launchers; each returns the launch status and enqueues only.

@@ -101,8 +101,10 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  * 32-key kernel, otherwise 64 (bf16) or 32 (fp32).  Built: for bf16 at
  * d = 64 and 128, 32 (a workgroup of 256 query rows in two wave groups that
  * alternate between matrix products and the softmax), 64 and 128 (128 query
- * rows); at d = 256, 32 and 64 (two stages of 128-key tiles would not fit in
- * LDS); 32 for fp32.  Other values give FA_ERR_UNSUPPORTED.
+ * rows, two LDS stages), 256 (one LDS stage: 128 KB of K and V at d = 128,
+ * so copies do not overlap work); at d = 256, 32 and 64 (two stages of
+ * 128-key tiles would not fit in LDS); 32 for fp32.  Other values give
+ * FA_ERR_UNSUPPORTED.
  * Results equal fa_fwd's up to rounding order.
  */
 fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -139,6 +141,23 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
                  int B, int H, int N, int d, int causal, float scale,
                  const int32_t *kv_lens, fa_dtype dtype, void *workspace,
                  size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * fa_bwd with an explicit tile length tile_n for the keys-outer dK/dV
+ * kernel: the query rows of each Q and dO tile it streams through LDS past
+ * its resident keys (the B_r of the pages' block-size constraint
+ * B_r*d + 2*B_c*d <= M, "FlashAttention: Mathematical Foundations ...",
+ * section "IO-Aware Tiling Algorithm", on the backward's side).
+ * tile_n = 0 picks the default (64); 64 is built at d = 64, 128, 256 and 128
+ * at d = 64, 128 (two stages of 128-row Q and dO tiles at d = 256 would need
+ * 256 KB of LDS).  Other values give FA_ERR_UNSUPPORTED.  Other arguments and
+ * errors as fa_bwd; results equal fa_bwd's up to rounding order.
+ */
+fa_status fa_bwd_ex(const void *q, const void *k, const void *v, const void *o,
+                    const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                    int B, int H, int N, int d, int causal, float scale,
+                    const int32_t *kv_lens, fa_dtype dtype, int tile_n, void *workspace,
+                    size_t workspace_bytes, fa_stream_t stream);
 
 /*
  * fa_bwd for callers that cannot allocate device memory (code under HIP

@@ -94,6 +94,7 @@ def test_fwd_rejects(lib, kw, want):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(tile=48), UNSUPPORTED), (dict(tile=512), UNSUPPORTED), (dict(tile=-1), UNSUPPORTED),
+    (dict(tile=256, d=256), UNSUPPORTED), (dict(tile=256, dtype=FP32), UNSUPPORTED),
     (dict(tile=64, dtype=FP32), UNSUPPORTED), (dict(tile=16, dtype=FP32), UNSUPPORTED),
     (dict(tile=64, d=80), UNSUPPORTED), (dict(tile=64, q=None), INVALID),
     (dict(tile=128, d=256), UNSUPPORTED), (dict(tile=16, d=128), UNSUPPORTED),
@@ -318,4 +319,21 @@ def test_bwd_noalloc_limit(lib):
 ])
 def test_bwd_noalloc_rejects(lib, kw, want):
     assert noalloc(lib, **kw) == want
+
+
+def bwd_ex(lib, tile, q=P, B=1, H=2, N=256, d=64, dtype=BF16, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    return lib.fa_bwd_ex(q, P, P, P, P, P, P, P, P, B, H, N, d, 0, 0.125, None, dtype, tile, ws,
+                         ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(tile=32), UNSUPPORTED), (dict(tile=256), UNSUPPORTED), (dict(tile=-1), UNSUPPORTED),
+    (dict(tile=128, d=256), UNSUPPORTED), (dict(tile=64, dtype=FP32), UNSUPPORTED),
+    (dict(tile=128, q=None), INVALID), (dict(tile=128, ws=None), WORKSPACE),
+    (dict(tile=64, ws_bytes=16), WORKSPACE),
+])
+def test_bwd_ex_rejects(lib, kw, want):
+    assert bwd_ex(lib, **kw) == want
 
