@@ -44,7 +44,7 @@ HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 # kernel name (as rocprofv3 reports it) -> source file, for the traffic
 # summaries' staleness check
 KERNEL_SOURCES = {
-    "fwd": "exact_io_aware_36_amd/csrc/fa_fwd.hip",
+    "fwd": ("exact_io_aware_36_amd/csrc/fa_fwd.hip", "exact_io_aware_36_amd/csrc/fa_fwd_pp.hip"),
     "bwd_dot": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
     "bwd_dkdv": "exact_io_aware_36_amd/csrc/fa_bwd_dkdv.hip",
     "bwd_dq": "exact_io_aware_36_amd/csrc/fa_bwd.hip",
@@ -514,6 +514,251 @@ def bench_io_ablation(args, fa, torch):
     return 0
 
 
+def _timed(torch, stream, fn, warmup, reps):
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def metric_range(fa, torch, steps=5, warmup=2, ds=(64, 128)):
+    """The metric's range, compactly: N = 256 ... 16384 with 16384 tokens per
+    batch (B = 16384 / N), H = 16, d = 64 and 128, causal and not; for each
+    point the forward alone and forward + backward (default kernels), HIP
+    events over `steps` calls.  Inputs N(0,1) x 0.5 (dO N(0,1)) drawn on the
+    GPU from a fixed seed (timing only; parity is tested elsewhere)."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    out = []
+    for d in ds:
+        for N in (256, 512, 1024, 2048, 4096, 8192, 16384):
+            B, H = max(1, 16384 // N), 16
+            gen.manual_seed(3000 + N + d)
+            shape = (B, H, N, d)
+            q, k, v = ((torch.randn(shape, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+                       for _ in range(3))
+            do = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+            ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+            for causal in (False, True):
+                def fwd():
+                    fa.fa_fwd(q, k, v, o, lse, causal=causal)
+
+                def step():
+                    fwd()
+                    fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=causal)
+
+                f = fwd_flops(B, H, N, d, causal)
+                t_f = _timed(torch, stream, fwd, warmup, steps)
+                t_s = _timed(torch, stream, step, warmup, steps)
+                out.append({"N": N, "d": d, "B": B, "causal": causal, "fwd_ms": round(t_f, 4),
+                            "fwd_tflops": round(f / (t_f * 1e-3) / 1e12, 1),
+                            "fwd_pct_peak": round(100 * f / (t_f * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
+                            "fwd_bwd_ms": round(t_s, 4),
+                            "fwd_bwd_tflops": round(2.5 * f / (t_s * 1e-3) / 1e12, 1)})
+            del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
+
+
+def other_configs(fa, torch, workloads, steps=10, warmup=3):
+    """The other measured workloads once each (default kernels, their seeded
+    inputs): the single-head fp32 forward, the GPT-2-shaped causal forward,
+    the BERT-shaped padded forward + backward and the block-sparse forward;
+    metric-convention TFLOP/s and per-stage times."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name in ("single_head_fp32", "gpt2_medium_causal", "bert_large_padded", "block_sparse"):
+        w = workloads.WORKLOADS[name]
+        inp = workloads.make_inputs(w)
+        B, H, N, d = inp["B"], inp["H"], inp["N"], inp["d"]
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        lens = inp["kv_lens"].to(dev) if inp["kv_lens"] is not None else None
+        mask = inp["block_mask"].to(dev) if inp["block_mask"] is not None else None
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+        def fwd():
+            if mask is not None:
+                fa.fa_fwd_blocksparse(q, k, v, o, lse, mask, mask_block=w.mask_block, scale=w.scale)
+            else:
+                fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=lens)
+
+        t_f = _timed(torch, stream, fwd, warmup, steps)
+        ff = fwd_flops(B, H, N, d, w.causal, w.sparse_frac)
+        r = {"fwd_ms": round(t_f, 4), "fwd_tflops": round(ff / (t_f * 1e-3) / 1e12, 2)}
+        if w.backward:
+            do = inp["dout"].to(dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+            ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+
+            def step():
+                fwd()
+                fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
+                          kv_lens=lens)
+
+            t_s = _timed(torch, stream, step, warmup, steps)
+            r.update({"fwd_bwd_ms": round(t_s, 4),
+                      "fwd_bwd_tflops": round(2.5 * ff / (t_s * 1e-3) / 1e12, 2)})
+        res[name] = r
+    return res
+
+
+# ---------------------------------------------------------------------------
+# profiler summaries: rocprofv3 CSVs (under gpurun_out/) -> profiles/*.txt
+
+DIGEST_PATTERNS = {"fwd": ["fwd_bf16_kernel", "fwd_pp_kernel", "fwd_bf16_t256_kernel"],
+                   "bwd_dot": ["bwd_dot_kernel"], "bwd_dkdv": ["bwd_dkdv_kernel"],
+                   "bwd_dq": ["bwd_dq_kernel"],
+                   "bwd_sparse": ["bwd_dot_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
+                   "fwd_fp8": ["fwd_fp8_kernel"], "decode": ["decode_kernel", "merge_kernel"]}
+SQ_GROUP = ("GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+            "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS")
+
+
+def _short_kernel(name):
+    import re
+    import subprocess
+
+    if name.startswith("_Z"):
+        name = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip() or name
+    name = re.sub(r"^void ", "", name).replace("(anonymous namespace)::", "")
+    return re.sub(r"\([^()]*\)$", "", name)
+
+
+def digest(workload, stages, root=ROOT, steps=10, warmup=3):
+    """Write profiles/kernel_stats_<workload>.txt from the kernel trace of
+    `rocprofv3 --kernel-trace --stats ... -o <workload> -- python3 bench.py
+    --workload <workload> --steps 10 --warmup 3 --quick` (stdout of that run
+    in gpurun_out/<workload>_stats.log), and for each stage
+    profiles/traffic_<stage>_<workload>.txt from three counter runs
+    (<workload>_p1: FETCH_SIZE, _p2: WRITE_SIZE, _p3: the SQ group) of
+    `bench.py --workload <workload> --steps 2 --warmup 1 --quick
+    --copy-calibration 512`, the counters scaled by what they read for the
+    512 MiB copy."""
+    import csv
+    from collections import defaultdict
+
+    import workloads
+
+    w = workloads.WORKLOADS[workload]
+    go = os.path.join(root, "gpurun_out")
+    wdesc = (f"B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} {'causal' if w.causal else 'non-causal'}"
+             + (f", kv_len U{{{w.kv_len_range[0]}..{w.kv_len_range[1]}}}" if w.kv_len_range else "")
+             + (", block mask" if w.sparse_frac else "") + (", fp8" if w.fp8 else ""))
+    trace_csv = os.path.join(go, "prof", f"{workload}_kernel_trace.csv")
+    if os.path.exists(trace_csv):
+        per = defaultdict(list)
+        for r in csv.DictReader(open(trace_csv)):
+            if "fa::" in r["Kernel_Name"] or r["Kernel_Name"].startswith("_ZN2fa"):
+                per[_short_kernel(r["Kernel_Name"])].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        tot = sum(sum(v) for v in per.values())
+        line = None
+        for ln in open(os.path.join(go, f"{workload}_stats.log")):
+            if ln.startswith("{"):
+                line = json.loads(ln)
+        det = line["detail"] if line else {}
+        ev = (", ".join(f"{k} {v}" for k, v in det["stage_ms"].items()) if "stage_ms" in det
+              else f"whole call {det.get('call_ms')}")
+        out = [f"# rocprofv3 kernel statistics: {workload} ({wdesc})",
+               "# command (from the repository root, on one MI355X):",
+               f"#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o {workload} "
+               f"-- python3 bench.py --workload {workload} --steps {steps} --warmup {warmup} --quick",
+               f"# summary: python3 bench.py --digest {workload} (CPU; reads gpurun_out/)",
+               f"# {steps + warmup} calls per kernel = {warmup} warm-up + {steps} timed steps. Durations in microseconds.",
+               f"# HIP-event averages over the timed steps printed by that same bench run (ms): {ev}",
+               "# timed_avg_us: average over the last calls (the timed steps), from the kernel trace of the same run.",
+               "",
+               f"{'kernel':<60}{'calls':>6}{'avg_us':>11}{'min_us':>11}{'max_us':>11}{'pct':>7}{'timed_avg_us':>14}"]
+        for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            tv = v[-steps:]
+            out.append(f"{k:<60}{len(v):>6}{sum(v)/len(v):>11.1f}{min(v):>11.1f}{max(v):>11.1f}"
+                       f"{100*sum(v)/tot:>7.2f}{sum(tv)/len(tv):>14.1f}")
+        with open(os.path.join(root, "profiles", f"kernel_stats_{workload}.txt"), "w") as f:
+            f.write("\n".join(out) + "\n")
+        print("\n".join(out))
+
+    def rows(p):
+        return list(csv.DictReader(open(os.path.join(go, "pmc", f"{workload}_p{p}_counter_collection.csv"))))
+
+    def per_launch(rs, pats, counter):
+        d = defaultdict(float)
+        names = {}
+        for r in rs:
+            if r["Counter_Name"] == counter and any(pt in r["Kernel_Name"] for pt in pats):
+                d[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = _short_kernel(r["Kernel_Name"])
+        by = defaultdict(list)
+        for k, v in d.items():
+            by[names[k]].append(v)
+        return sum(sum(v) / len(v) for v in by.values()), sorted(by)
+
+    def copy_kib(rs, counter):
+        return max((float(r["Counter_Value"]) for r in rs
+                    if r["Counter_Name"] == counter and "copy" in r["Kernel_Name"].lower()), default=0.0)
+
+    if not stages:
+        return
+    p1, p2, p3 = rows(1), rows(2), rows(3)
+    cf, cw = copy_kib(p1, "FETCH_SIZE"), copy_kib(p2, "WRITE_SIZE")
+    ff, fw = 512 * 1024 / cf, 512 * 1024 / cw
+    for stage in stages:
+        pats = DIGEST_PATTERNS[stage]
+        fetch, kn = per_launch(p1, pats, "FETCH_SIZE")
+        write, _ = per_launch(p2, pats, "WRITE_SIZE")
+        c3 = {c: per_launch(p3, pats, c)[0] for c in SQ_GROUP.split()}
+        if stage == "decode":
+            lens = workloads.make_inputs(w)["kv_lens"].numpy()
+            floor = decode_accounting(w.B, w.H, w.nq, w.d, lens, w.causal)[1]
+        else:
+            floor = floor_bytes(stage, w.B, w.H, w.N, w.d)
+        hbm = fetch * 1024 * ff + write * 1024 * fw
+        what = "one launch" if len(kn) == 1 else f"one call (its {len(kn)} launches)"
+        cmd = [f"#   rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc -o {workload}_p{i} -- "
+               f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --quick --copy-calibration 512"
+               for i, c in ((1, "FETCH_SIZE"), (2, "WRITE_SIZE"), (3, SQ_GROUP))]
+        busy = c3["SQ_BUSY_CU_CYCLES"]
+        out = [f"# HBM traffic of {what} of the {stage} stage ({' + '.join(kn)}), {workload}",
+               f"# ({wdesc}), from rocprofv3 counters.",
+               "# commands (from the repository root, on one MI355X; one counter group per run):", *cmd,
+               f"# summary: python3 bench.py --digest {workload} {stage} (CPU; reads gpurun_out/)",
+               "# Scaling: the same runs first copy 512 MiB with a plain device copy; its counters read",
+               f"# FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB for 524288 KiB moved each way, so",
+               f"# FETCH_SIZE is multiplied by {ff:.4f} and WRITE_SIZE by {fw:.4f}.",
+               "# source_sha256 is the first 16 hex digits of the sha256 over the kernel source, the two shared",
+               "# kernel headers and the build script (compiler flags) when measured; bench.py reports this",
+               "# traffic only while they are unchanged.",
+               f"source_sha256: {source_digest(KERNEL_SOURCES[stage])}",
+               f"fetch_size_kib_per_launch: {fetch:.1f}",
+               f"write_size_kib_per_launch: {write:.1f}",
+               f"fetch_bytes_scaled: {fetch*1024*ff:.0f}",
+               f"write_bytes_scaled: {write*1024*fw:.0f}",
+               f"hbm_bytes_per_launch: {hbm:.0f}",
+               f"floor_bytes_per_launch: {floor:.0f}   # O(Nd) inputs + outputs once",
+               f"ratio_to_floor: {hbm/floor:.3f}",
+               f"mfma_busy_fraction: {c3['SQ_VALU_MFMA_BUSY_CYCLES']/(4*busy) if busy else 0:.3f}"
+               "   # SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES)",
+               f"busy_cycles_per_cu: {busy/256:.3g}",
+               f"gpu_clock_cycles_per_xcd: {c3['GRBM_GUI_ACTIVE']/8:.4g}   # GRBM_GUI_ACTIVE / 8 XCDs",
+               f"insts_valu: {c3['SQ_INSTS_VALU']:.4g}",
+               f"insts_mfma: {c3['SQ_INSTS_MFMA']:.4g}",
+               f"insts_lds: {c3['SQ_INSTS_LDS']:.4g}",
+               f"lds_bank_conflict_cycles: {c3['SQ_LDS_BANK_CONFLICT']:.0f}",
+               f"wait_inst_lds: {c3['SQ_WAIT_INST_LDS']:.4g}"]
+        with open(os.path.join(root, "profiles", f"traffic_{stage}_{workload}.txt"), "w") as f:
+            f.write("\n".join(out) + "\n")
+        print("\n".join(out))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,8 +766,16 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_context_causal")
     ap.add_argument("--tile", type=int, default=0, help="forward key tile (0 = default)")
-    ap.add_argument("--tile-sweep", default="64,128",
+    ap.add_argument("--tile-sweep", default="32,64,128,256",
                     help="forward key tiles to time on the side ('' to skip)")
+    ap.add_argument("--bwd-tile-sweep", default="64,128",
+                    help="backward (dK/dV query) tiles to time on the side ('' to skip)")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the workload's own step: no tile sweeps, no metric range, no other "
+                         "workloads, no CPU baseline (for profiler runs)")
+    ap.add_argument("--digest", nargs="+", metavar=("WORKLOAD", "STAGE"),
+                    help="instead of running: summarise rocprofv3 CSVs under gpurun_out/ into "
+                         "profiles/ (CPU only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true",
@@ -536,6 +789,13 @@ def main(argv=None):
                          "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
 
+    if args.digest:
+        digest(args.digest[0], args.digest[1:])
+        return 0
+    if args.quick:
+        args.tile_sweep = ""
+        args.bwd_tile_sweep = ""
+        args.no_cpu_baseline = True
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(heads and batch shard across GPUs with no communication; see the design notes)",
@@ -655,6 +915,8 @@ def main(argv=None):
     sweep = [int(t) for t in args.tile_sweep.split(",") if t.strip()] if mask is None else []
     if d == 256 and sweep:   # the key tiles built at head dim 256
         sweep = [32, 64]
+    if w.dtype != "bf16":
+        sweep = []
     if sweep:
         res = {}
         for t in sweep:
@@ -670,6 +932,25 @@ def main(argv=None):
             ms = e0.elapsed_time(e1) / reps
             res[str(t)] = {"fwd_ms": round(ms, 4), "fwd_tflops": round(fflops / (ms * 1e-3) / 1e12, 2)}
         detail["fwd_tile_sweep"] = res
+    bsweep = [int(t) for t in args.bwd_tile_sweep.split(",") if t.strip()]
+    if w.backward and mask is None and bsweep:
+        res = {}
+        for t in bsweep:
+            if d == 256 and t != 64:
+                continue
+
+            def bwd_call(t=t):
+                fa.fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
+                             kv_lens=lens, tile_n=t)
+
+            ms = _timed(torch, stream, bwd_call, 3, max(3, args.steps // 2))
+            res[str(t)] = {"bwd_ms": round(ms, 4),
+                           "bwd_tflops_2.5x": round(2.5 * fflops / (ms * 1e-3) / 1e12, 2),
+                           "fwd_bwd_tflops": round(2.5 * fflops / ((ms + stage_ms["fwd"]) * 1e-3) / 1e12, 2)}
+        detail["bwd_tile_sweep"] = res
+    if not args.quick and args.workload == "long_context_causal":
+        detail["sweep"] = metric_range(fa, torch)
+        detail["configs"] = other_configs(fa, torch, workloads)
 
     cpu = None
     if not args.no_cpu_baseline:
