@@ -24,7 +24,7 @@ import torch
 import oracle
 import workloads
 from oracle import fp8 as ofp8
-from test_parity_gpu import LSE_MAX_ABS, check_lse, half_ulp_bf16, host, say
+from test_parity_gpu import half_ulp_bf16, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,19 @@ def check_bound(name, gpu, ref, bound):
     rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30))
     say(f"    {name}: max_abs={err.max():.3e} max(err/bound)={float((err / np.maximum(bound + half_ulp_bf16(ref), 1e-30)).max()):.3f} rel_l2={rel:.3e}")
     assert excess.max() <= 0.0, f"{name}: error exceeds the E4M3 probability bound by {excess.max()}"
+
+
+def check_lse_bound(name, gpu, ref, bound):
+    """FP8 LSE against the bound derived from the E4M3 product sums' measured
+    truncation and the fp32 work after them (oracle.fp8.lse_bound_rows)."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert (np.isneginf(gpu) == np.isneginf(ref)).all(), f"{name}: -inf rows differ"
+    fin = np.isfinite(ref)
+    err = np.abs(np.where(fin, gpu - ref, 0.0))
+    ratio = float((err / np.maximum(bound, 1e-30))[fin].max()) if fin.any() else 0.0
+    say(f"    {name}: max_abs={err.max():.3e} max(err/bound)={ratio:.3f} max bound={bound.max():.3e}")
+    assert np.all(err[fin] <= bound[fin]), f"{name}: LSE error exceeds its bound ({ratio:.3f} of it)"
 
 
 def qkv(B, H, N, d, seed, outliers=False):
@@ -117,9 +130,10 @@ def test_fwd_fp8_small(fa, shape, causal, padded):
     o, lse = run_fp8(fa, q8, qs, k8, ks, v8, vs, causal, lens)
     O, L, (Q, K, V) = ofp8.reference(q8, k8, v8, qs, ks, vs, causal=causal,
                                      kv_lens=None if lens is None else lens.numpy())
-    bound = ofp8.p_quant_bound(Q, K, V, L, causal=causal, kv_lens=None if lens is None else lens.numpy())
+    kvl = None if lens is None else lens.numpy()
+    bound = ofp8.p_quant_bound(Q, K, V, L, causal=causal, kv_lens=kvl)
     check_bound("O", o, O, bound)
-    check_lse("LSE", lse, L)
+    check_lse_bound("LSE", lse, L, ofp8.lse_bound(q8, qs, k8, ks, L, causal=causal, kv_lens=kvl))
 
 
 def test_fwd_fp8_deterministic(fa):
@@ -168,4 +182,6 @@ def test_workload_long_context_fp8(fa):
         bound = ofp8.p_quant_bound_rows(Q[0, h, rows], rows, K[0, h], V[0, h], Lr, causal=True,
                                         scale=w.scale)
         check_bound(f"O[h={h}]", o[0, h, rows], Or, bound)
-        check_lse(f"LSE[h={h}]", lse[0, h, rows], Lr)
+        lb = ofp8.lse_bound_rows(q8[0, h, rows], rows, qs[0, h, rows // 128], k8[0, h],
+                                 ks[0, h, np.arange(N) // 128], Lr, causal=True, scale=w.scale)
+        check_lse_bound(f"LSE[h={h}]", lse[0, h, rows], Lr, lb)

@@ -164,3 +164,81 @@ def test_p_rounding_bound_is_nearly_attained():
     Osim = pq.sum() / pt.astype(np.float64).sum()
     err = abs(Osim - O[0, 0, 1, 0])
     assert err <= bound[0, 0, 1, 0] and err >= 0.9 * bound[0, 0, 1, 0]
+
+
+def simulate_scores(q8, k8, window=14):
+    """The measured arithmetic of the E4M3 product sum, written directly: per
+    64-product block every product truncated toward zero to a multiple of
+    2^(E - window) (E = binade of the block's largest |product|), the
+    block's sum added to an fp32 accumulator."""
+    a = fp8.e4m3_decode(q8).astype(np.float64)
+    b = fp8.e4m3_decode(k8).astype(np.float64)
+    n, d = a.shape
+    acc = np.zeros((n, b.shape[0]), dtype=np.float32)
+    for c in range(0, d, 64):
+        p = a[:, None, c:c + 64] * b[None, :, c:c + 64]
+        mx = np.abs(p).max(axis=-1, keepdims=True)
+        e = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
+        lsb = np.exp2(e - window)
+        t = np.trunc(p / lsb) * lsb
+        acc = (acc.astype(np.float64) + t.sum(axis=-1)).astype(np.float32)
+    return acc.astype(np.float64)
+
+
+def lse_of(s):
+    m = s.max(axis=1, keepdims=True)
+    return (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+
+
+@pytest.mark.parametrize("kind", ["random", "aligned", "spread"])
+def test_lse_bound_holds_for_a_direct_simulation(kind):
+    """Scores from the simulated E4M3 product sums against exact ones: the LSE
+    difference stays within lse_bound_rows (for random codes; for queries and
+    keys along one direction, with scores ramping up to ~80 nats; and with
+    every key near 80 nats, so that the probability -- and the error LSE
+    inherits from every score -- is spread over all keys)."""
+    rng = np.random.default_rng(5)
+    n, N, d = 48, 96, 128
+    if kind == "random":
+        q = rng.standard_normal((n, d)) * 3
+        k = rng.standard_normal((N, d)) * 3
+    else:
+        u = rng.standard_normal(d)
+        u /= np.linalg.norm(u)
+        q = 4 * u + 0.05 * rng.standard_normal((n, d)) / np.sqrt(d)
+        top = np.linspace(0, 120, N) if kind == "aligned" else np.full(N, 115.0)
+        k = (top / (4 / np.sqrt(d) * 1.4426950408889634))[:, None] * u \
+            + 0.05 * rng.standard_normal((N, d)) / np.sqrt(d)
+    q8, qs = fp8.quantize(q[None, None], 0)
+    k8, ks = fp8.quantize(k[None, None], 0)
+    q8, k8 = q8[0, 0], k8[0, 0]
+    craw = (1 / np.sqrt(d)) * float(qs[0, 0, 0]) * float(ks[0, 0, 0])
+    exact = craw * (fp8.e4m3_decode(q8) @ fp8.e4m3_decode(k8).T)
+    sim = craw * simulate_scores(q8, k8)
+    L = lse_of(exact)
+    bound = fp8.lse_bound_rows(q8, np.arange(n), np.full(n, qs[0, 0, 0]), k8, np.full(N, ks[0, 0, 0]), L)
+    err = np.abs(lse_of(sim) - L)
+    assert np.all(err <= bound), (kind, float((err / bound).max()))
+    print(kind, float(np.abs(exact).max()), float(err.max()), float((err / bound).max()))
+    if kind != "random":
+        assert float(np.abs(exact).max()) > 70          # the large-score regime
+        assert float((err / bound).max()) > 0.05        # not vacuous there
+
+
+def test_score_bound_is_nearly_attained():
+    """One product 2^7 and 63 products whose lowest bit lies one place below
+    the 14-bit window: each loses exactly that bit, 63 * 2^(E - 15) in all,
+    a quarter of the bound's 63 * 2^(E - 13); one bit more of window in the
+    bound (2^(E - 14)) would leave only twice the truncation."""
+    a = np.zeros((1, 64), np.float32)
+    b = np.zeros((1, 64), np.float32)
+    a[0, 0], b[0, 0] = 16.0, 8.0                                     # 2^7, exact
+    a[0, 1:], b[0, 1:] = 1.875 * 2.0 ** -4, 1.875 * 2.0 ** -4         # 3.515625 * 2^-8 each
+    q8, k8 = fp8.e4m3_encode(a), fp8.e4m3_encode(b)
+    exact = float((fp8.e4m3_decode(q8) @ fp8.e4m3_decode(k8).T)[0, 0])
+    sim = float(simulate_scores(q8, k8)[0, 0])
+    err = exact - sim
+    bound = float(fp8.score_error_bound(q8, k8)[0, 0])
+    assert err > 0 and err <= bound
+    assert err >= 0.2 * bound, (err, bound)
+

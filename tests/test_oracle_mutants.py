@@ -66,6 +66,9 @@ MUTANTS = [
                                 "return np.float32(1.0)")]),
     ("rotation_butterfly_sign", PY, [("v[..., 1, :] = a - b", "v[..., 1, :] = b - a")]),
     ("probability_bound_halved", PY, [("w = np.maximum(2.0 ** -4 * P,", "w = np.maximum(2.0 ** -5 * P,")]),
+    ("score_truncation_window_too_narrow", PY, [("WINDOW_BITS = 13", "WINDOW_BITS = 18")]),
+    ("lse_bound_weights_dropped", PY, [("first = 1.05 * (P * delta).sum(axis=1)",
+                                        "first = 1.05 * (P * delta).max(axis=1)")]),
 ]
 
 
