@@ -9,7 +9,8 @@ Bars (written here, applied per output tensor):
   LSE (fp32): max abs <= 1e-3;
   fp32 path: O and LSE max abs <= 1e-5.
 Small cases span several tiles and a ragged tail; the five measured workloads
-run at full size (sampled rows where the oracle would be too slow).
+run at full size, every element compared (the long-context case also has a
+faster check on sampled rows, used for its tile variants).
 """
 from __future__ import annotations
 
@@ -353,6 +354,30 @@ def test_workload_long_context_causal(fa):
         check_bf16(f"dV[h={h}]", host(dv)[0, h, kr], sv)
 
 
+@pytest.mark.timeout(900)
+def test_workload_long_context_causal_full(fa):
+    """The same long-context causal forward and backward compared on every
+    element: O, LSE, dQ, dK and dV of all 16 heads against the oracle's full
+    fp64 forward and backward (about a minute of CPU time on 16 cores)."""
+    w = workloads.WORKLOADS["long_context_causal"]
+    inp = workloads.make_inputs(w)
+    say(f"  {w.name} full tensors (oracle on {oracle.threads()} threads)")
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["dout"])
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (host(t) for t in (o, lse, dq, dk, dv))
+    qf, kf, vf, dof = (f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    O, L = oracle.fwd(qf, kf, vf, causal=True, scale=w.scale)
+    check_bf16("O", o, O)
+    check_lse("LSE", lse, L)
+    del O, L
+    dQ, dK, dV, _ = oracle.bwd(qf, kf, vf, dof, causal=True, scale=w.scale)
+    check_bf16("dQ", dq, dQ)
+    check_bf16("dK", dk, dK)
+    check_bf16("dV", dv, dV)
+
+
 @pytest.mark.parametrize("tile_n", [64, 128])
 def test_workload_long_context_bwd_tiles(fa, tile_n):
     """The backward's query-tile choices at the long-context size (two
@@ -393,10 +418,11 @@ def test_workload_long_context_tiles(fa, tile_n):
     check_lse("LSE[rows]", host(lse).reshape(-1)[rows], Lr)
 
 
+@pytest.mark.timeout(600)
 def test_workload_block_sparse_backward(fa):
     """The block-sparse workload with a backward pass (dO drawn after Q, K,
-    V from the same seed): the oracle checks dQ on 64 query rows and dK, dV on
-    64 key rows of two heads."""
+    V from the same seed): dQ, dK and dV compared on every element with the
+    oracle's full backward under the same block mask."""
     w = workloads.WORKLOADS["block_sparse_fwdbwd"]
     inp = workloads.make_inputs(w)
     say(f"  {w.name}")
@@ -406,17 +432,12 @@ def test_workload_block_sparse_backward(fa):
     o, lse = fa.fwd_blocksparse(q, k, v, dm)
     dq, dk, dv = fa.bwd_blocksparse(q, k, v, o, do, lse, dm)
     torch.cuda.synchronize()
-    B, H, N, d = q.shape
-    rng = np.random.default_rng(5)
     qf, kf, vf, dof = (f64(inp[n]) for n in ("q", "k", "v", "dout"))
-    for b, h in ((0, 0), (B - 1, H - 1)):
-        qr = np.concatenate([[0, N - 1], rng.choice(N, 62, replace=False)])
-        kr = np.concatenate([[0, N - 1], rng.choice(N, 62, replace=False)])
-        sq, sk, sv = oracle.bwd_sample(qf[b, h], kf[b, h], vf[b, h], dof[b, h], qr, kr,
-                                       scale=w.scale, block_mask=mask.numpy(), mask_block=128)
-        check_bf16(f"dQ[{b},{h}]", host(dq)[b, h, qr], sq)
-        check_bf16(f"dK[{b},{h}]", host(dk)[b, h, kr], sk)
-        check_bf16(f"dV[{b},{h}]", host(dv)[b, h, kr], sv)
+    dQ, dK, dV, _ = oracle.bwd(qf, kf, vf, dof, scale=w.scale, block_mask=mask.numpy(),
+                               mask_block=128)
+    check_bf16("dQ", host(dq), dQ)
+    check_bf16("dK", host(dk), dK)
+    check_bf16("dV", host(dv), dV)
 
 
 def test_workload_block_sparse(fa):
