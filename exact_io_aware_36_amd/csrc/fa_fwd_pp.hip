@@ -17,14 +17,16 @@
 // apart, every phase ending at a workgroup barrier, so that on each SIMD one
 // wave runs matrix products while the other runs everything else:
 //
-//   MFMA block t:  S_t = K_t Q^T and O^T += V_{t-1}^T P_{t-1}^T, operands
-//                  already in registers: back-to-back MFMAs, no LDS reads.
+//   MFMA block t:  S_t = K_t Q^T and O^T += V_{t-1}^T P_{t-1}^T from operands
+//                  already in registers, with the LDS reads of the next MFMA
+//                  block's operands (K_{t+1}, V_t) issued between the products.
 //   VALU block t:  softmax of S_t -> P_t (masks, lazy rescale, row sums), the
-//                  LDS reads of the next MFMA block's operands (V_t, K_{t+1}),
-//                  the buffer->LDS copy of a tile NST - 1 ahead.
+//                  buffer->LDS copy of a tile NST - 1 ahead, a wait for the
+//                  copy three tiles ahead.
 //
-// The exponentials, LDS reads and copies of one wave thus overlap the other
-// wave's matrix products instead of taking turns with its own.  Key tiles of
+// The exponentials and copies of one wave thus overlap the other wave's
+// matrix products instead of taking turns with its own, and a block's reads
+// have a whole phase to land before their products.  Key tiles of
 // BC keys pass through NST LDS stages; a tile's stage is refilled once both
 // groups have read its V (two phases after its K).  One workgroup per CU
 // (512 threads, up to 256 registers per lane).
