@@ -75,7 +75,8 @@ def check_lse(name, gpu, ref, tol=LSE_MAX_ABS):
     ref = np.asarray(ref, np.float64)
     both_inf = np.isneginf(gpu) & np.isneginf(ref)
     assert (np.isneginf(gpu) == np.isneginf(ref)).all(), f"{name}: -inf rows differ"
-    d = np.abs(np.where(both_inf, 0.0, gpu - ref))
+    with np.errstate(invalid="ignore"):      # -inf - -inf where both rows saw no key
+        d = np.abs(np.where(both_inf, 0.0, gpu - ref))
     say(f"    {name}: max_abs={d.max() if d.size else 0:.3e}")
     assert d.max() <= tol, f"{name}: {d.max()} > {tol}"
 
