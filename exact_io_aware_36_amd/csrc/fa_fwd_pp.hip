@@ -487,19 +487,21 @@ hipError_t launch_pp_inst(const FwdArgs &a, hipStream_t s)
 
 } // namespace
 
-#ifndef FA_PP_NST
-#define FA_PP_NST 6
-#endif
+// LDS stages of the copy ring.  Measured at d = 128 against 4 and 8 stages
+// (alternating timings, B1 H16 N16384 to B8 H16 N2048, causal and not): 8 is
+// about 1 % slower everywhere, 4 is 2-18 % slower except non-causal
+// N = 16384, so 6 (96 KB of LDS).
+constexpr int kPpStages = 6;
 
 // two-group forward: d = 64 or 128, 32-key tiles
 hipError_t launch_fwd_pp(const FwdArgs &a, int d, bool causal, hipStream_t s)
 {
     if (d == 128)
-        return causal ? launch_pp_inst<128, 32, FA_PP_NST, true>(a, s)
-                      : launch_pp_inst<128, 32, FA_PP_NST, false>(a, s);
+        return causal ? launch_pp_inst<128, 32, kPpStages, true>(a, s)
+                      : launch_pp_inst<128, 32, kPpStages, false>(a, s);
     if (d == 64)
-        return causal ? launch_pp_inst<64, 32, FA_PP_NST, true>(a, s)
-                      : launch_pp_inst<64, 32, FA_PP_NST, false>(a, s);
+        return causal ? launch_pp_inst<64, 32, kPpStages, true>(a, s)
+                      : launch_pp_inst<64, 32, kPpStages, false>(a, s);
     return hipErrorInvalidValue;
 }
 
