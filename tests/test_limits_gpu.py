@@ -9,7 +9,12 @@
   * block-sparse forward and backward at N = 65536 (the largest the API
     takes) with a block-diagonal mask: every 128-row block is then an
     independent attention problem, which the oracle solves exactly for a
-    few blocks.
+    few blocks;
+  * the dense forward (every key tile) and backward (both query tiles) with
+    B*H*N*d just under 2^31 elements (B = 1000, H = 16, N = 1024, d = 128:
+    3.9 GiB per tensor, byte offsets past 2^31, the last head 3.9 GiB in): every
+    (b, h) is an independent problem, so the oracle checks whole heads,
+    the last among them.
 """
 from __future__ import annotations
 
@@ -82,3 +87,52 @@ def test_blocksparse_largest_n(fa):
         check_bf16(f"dQ[blk {blk}]", host(dq)[:, :, sl], dQ)
         check_bf16(f"dK[blk {blk}]", host(dk)[:, :, sl], dK)
         check_bf16(f"dV[blk {blk}]", host(dv)[:, :, sl], dV)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_at_element_limit(fa, causal):
+    B, H, N, d = 1000, 16, 1024, 128
+    assert B * H * N * d < 2**31 and (B * H - 1) * N * d * 2 > 2**31
+    say(f"  dense B={B} H={H} N={N} d={d} causal={causal}: {B * H * N * d * 2 / 2**30:.2f} GiB per tensor")
+    gen = torch.Generator(device="cuda").manual_seed(2031 + causal)
+
+    def draw(scale):
+        return (torch.randn((B, H, N, d), generator=gen, device="cuda") * scale).to(torch.bfloat16)
+
+    q, k, v = draw(0.5), draw(0.5), draw(1.0)
+    do = draw(1.0)
+    heads = (0, 7777, B * H - 1)
+
+    def head(t, bh):
+        return t.view(B * H, N, d)[bh].double().cpu().numpy()[None, None]
+
+    refs = {}
+    for bh in heads:
+        qs, ks, vs, ds = head(q, bh), head(k, bh), head(v, bh), head(do, bh)
+        O, L = oracle.fwd(qs, ks, vs, causal=causal)
+        dQ, dK, dV, _ = oracle.bwd(qs, ks, vs, ds, causal=causal)
+        refs[bh] = (O, L, dQ, dK, dV)
+    o64 = lse64 = None
+    for tile in (32, 64, 128, 256):
+        say(f"    forward, key tile {tile}")
+        o, lse = fa.fwd(q, k, v, causal=causal, tile_n=tile)
+        torch.cuda.synchronize()
+        for bh in heads:
+            O, L = refs[bh][:2]
+            check_bf16(f"O[{bh}] tile={tile}", host(o.view(B * H, N, d)[bh])[None, None], O)
+            check_lse(f"LSE[{bh}] tile={tile}", host(lse.view(B * H, N)[bh])[None, None], L)
+        if tile == 64:
+            o64, lse64 = o, lse
+        del o, lse
+    for tile in (64, 128):
+        say(f"    backward, query tile {tile}")
+        dq, dk, dv = fa.bwd(q, k, v, o64, do, lse64, causal=causal, tile_n=tile)
+        torch.cuda.synchronize()
+        for bh in heads:
+            dQ, dK, dV = refs[bh][2:]
+            check_bf16(f"dQ[{bh}] tile={tile}", host(dq.view(B * H, N, d)[bh])[None, None], dQ)
+            check_bf16(f"dK[{bh}] tile={tile}", host(dk.view(B * H, N, d)[bh])[None, None], dK)
+            check_bf16(f"dV[{bh}] tile={tile}", host(dv.view(B * H, N, d)[bh])[None, None], dV)
+        del dq, dk, dv
+    del q, k, v, do, o64, lse64
+    torch.cuda.empty_cache()
