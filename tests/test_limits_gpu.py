@@ -14,7 +14,11 @@
     B*H*N*d just under 2^31 elements (B = 1000, H = 16, N = 1024, d = 128:
     3.9 GiB per tensor, byte offsets past 2^31, the last head 3.9 GiB in): every
     (b, h) is an independent problem, so the oracle checks whole heads,
-    the last among them.
+    the last among them;
+  * the FP8 quantiser and forward at the same size (1.95 GiB of codes per
+    tensor): the codes and descales of whole heads equal the oracle
+    quantiser's bit for bit, and the forward of those heads stays within the
+    derived E4M3 bounds.
 """
 from __future__ import annotations
 
@@ -25,7 +29,9 @@ import pytest
 import torch
 
 import oracle
+import oracle.fp8 as ofp8
 import workloads
+from test_fp8_gpu import check_bound, check_lse_bound
 from test_parity_gpu import check_bf16, check_lse, f64, host, say
 
 pytestmark = pytest.mark.gpu
@@ -135,4 +141,40 @@ def test_dense_at_element_limit(fa, causal):
             check_bf16(f"dV[{bh}] tile={tile}", host(dv.view(B * H, N, d)[bh])[None, None], dV)
         del dq, dk, dv
     del q, k, v, do, o64, lse64
+    torch.cuda.empty_cache()
+
+
+def test_fp8_at_element_limit(fa):
+    B, H, N, d = 1000, 16, 1024, 128
+    say(f"  fp8 B={B} H={H} N={N} d={d} causal: {B * H * N * d / 2**30:.2f} GiB of codes per tensor")
+    gen = torch.Generator(device="cuda").manual_seed(2033)
+
+    def draw(scale):
+        return (torch.randn((B, H, N, d), generator=gen, device="cuda") * scale).to(torch.bfloat16)
+
+    q, k, v = draw(0.5), draw(0.5), draw(1.0)
+    signs = workloads.random_signs(d, 2033)
+    q8, qs = fa.quantize_fp8(q, 128, signs=signs.cuda())
+    k8, ks = fa.quantize_fp8(k, 128, signs=signs.cuda())
+    v8t, vs = fa.quantize_fp8(v, 0, transpose=True)
+    o, lse = fa.fwd_fp8(q8, k8, v8t, qs, ks, vs, causal=True)
+    torch.cuda.synchronize()
+    nblk = N // 128
+    for bh in (0, 7777, B * H - 1):
+        x = {n: t.view(B * H, N, d)[bh].float().cpu().numpy()[None, None] for n, t in (("q", q), ("k", k), ("v", v))}
+        cq, dq_ = ofp8.quantize(x["q"], 128, signs.numpy())
+        ck, dk_ = ofp8.quantize(x["k"], 128, signs.numpy())
+        cv, dv_ = ofp8.quantize(x["v"], 0)
+        assert np.array_equal(q8.view(B * H, N, d)[bh].cpu().numpy(), cq[0, 0]), f"q codes of head {bh}"
+        assert np.array_equal(k8.view(B * H, N, d)[bh].cpu().numpy(), ck[0, 0]), f"k codes of head {bh}"
+        assert np.array_equal(v8t.view(B * H, d, N)[bh].cpu().numpy().T, cv[0, 0]), f"v codes of head {bh}"
+        assert np.array_equal(qs.view(B * H, nblk)[bh].cpu().numpy(), dq_.reshape(nblk))
+        assert np.array_equal(ks.view(B * H, nblk)[bh].cpu().numpy(), dk_.reshape(nblk))
+        assert np.array_equal(vs.view(B * H)[bh].cpu().numpy().reshape(1), dv_.reshape(1))
+        O, L, (Qd, Kd, Vd) = ofp8.reference(cq, ck, cv, dq_, dk_, dv_, causal=True)
+        check_bound(f"O[{bh}]", host(o.view(B * H, N, d)[bh])[None, None], O,
+                    ofp8.p_quant_bound(Qd, Kd, Vd, L, causal=True))
+        check_lse_bound(f"LSE[{bh}]", host(lse.view(B * H, N)[bh])[None, None], L,
+                        ofp8.lse_bound(cq, dq_, ck, dk_, L, causal=True))
+    del q, k, v, q8, k8, v8t, o, lse
     torch.cuda.empty_cache()
