@@ -15,6 +15,9 @@
     and 500 at d = 256: 3.9 GiB per tensor, byte offsets past 2^31): every
     (b, h) is an independent problem, so the oracle checks whole heads,
     the last among them;
+  * the block-sparse forward and backward at the same size (d = 128, a
+    random 8 x 8 mask of 128-blocks with its diagonal on), whole heads
+    against the oracle under the same mask;
   * the FP8 quantiser and forward at the same size (1.95 GiB of codes per
     tensor): the codes and descales of whole heads equal the oracle
     quantiser's bit for bit, and the forward of those heads stays within the
@@ -179,4 +182,36 @@ def test_fp8_at_element_limit(fa):
         check_lse_bound(f"LSE[{bh}]", host(lse.view(B * H, N)[bh])[None, None], L,
                         ofp8.lse_bound(cq, dq_, ck, dk_, L, causal=True))
     del q, k, v, q8, k8, v8t, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_blocksparse_at_element_limit(fa):
+    B, H, N, d = 1000, 16, 1024, 128
+    nb = N // 128
+    mask_np = workloads.random_block_mask(nb, 0.4, 2035).numpy()
+    say(f"  block-sparse B={B} H={H} N={N} d={d}: {int(mask_np.sum())} of {nb * nb} blocks on")
+    gen = torch.Generator(device="cuda").manual_seed(2035)
+
+    def draw(scale):
+        return (torch.randn((B, H, N, d), generator=gen, device="cuda") * scale).to(torch.bfloat16)
+
+    q, k, v, do = draw(0.5), draw(0.5), draw(1.0), draw(1.0)
+    dm = torch.from_numpy(mask_np).cuda()
+    o, lse = fa.fwd_blocksparse(q, k, v, dm)
+    dq, dk, dv = fa.bwd_blocksparse(q, k, v, o, do, lse, dm)
+    torch.cuda.synchronize()
+
+    def head(t, bh):
+        return t.view(B * H, N, d)[bh]
+
+    for bh in (0, 5555, B * H - 1):
+        qs, ks, vs, ds = (head(t, bh).double().cpu().numpy()[None, None] for t in (q, k, v, do))
+        O, L = oracle.fwd(qs, ks, vs, block_mask=mask_np, mask_block=128)
+        dQ, dK, dV, _ = oracle.bwd(qs, ks, vs, ds, block_mask=mask_np, mask_block=128)
+        check_bf16(f"O[{bh}]", host(head(o, bh))[None, None], O)
+        check_lse(f"LSE[{bh}]", host(lse.view(B * H, N)[bh])[None, None], L)
+        check_bf16(f"dQ[{bh}]", host(head(dq, bh))[None, None], dQ)
+        check_bf16(f"dK[{bh}]", host(head(dk, bh))[None, None], dK)
+        check_bf16(f"dV[{bh}]", host(head(dv, bh))[None, None], dV)
+    del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
