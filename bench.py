@@ -168,6 +168,28 @@ def read_traffic(stage: str, workload: str):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def percentiles(xs, qs=(10, 50, 90)):
+    """Nearest-rank percentiles of a list of floats."""
+    ys = sorted(xs)
+    out = {}
+    for q in qs:
+        i = min(len(ys) - 1, max(0, int(round(q / 100 * (len(ys) - 1)))))
+        out[q] = ys[i]
+    return out
+
+
 def cpu_baseline(inp, w, metric_flops, budget_s=15.0, seed=99):
     """Time the oracle on a random sample of query rows (forward rows, and for
     workloads with a backward also dQ of the same rows); credit the sample
@@ -214,6 +236,7 @@ def cpu_baseline(inp, w, metric_flops, budget_s=15.0, seed=99):
     flops = metric_flops * n / total_rows
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{n} of {total_rows} query rows drawn uniformly at random (batches of 64, 128, "
                    f"... until {budget_s:.0f} s): oracle fp64 forward "
                    f"rows{' + backward dQ rows' if w.backward else ''}, {dt:.1f} s; credited "
@@ -256,7 +279,7 @@ def cpu_baseline_decode(inp, w, budget_s=15.0):
     flops, _ = decode_accounting(inp["B"], inp["H"], w.nq, inp["d"],
                                  lens if lens is not None else [inp["N"]] * inp["B"], w.causal)
     return {"value": flops * reps / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"the whole workload, {reps} oracle fp64 decode call(s) in {dt:.1f} s",
             "seconds": dt}
 
@@ -900,8 +923,12 @@ def main(argv=None):
                 "avg_launch_ms": round(stage_ms[dom], 4)}
 
     fflops = fwd_flops(B, H, N, d, w.causal, sf)
+    # per-step spread from the same events (first stage's start to last stage's end)
+    step_ev = [evs[i][0].elapsed_time(evs[i][-1]) for i in range(args.steps)]
+    pc = percentiles(step_ev)
     detail = {
         "stage_ms": {s: round(t, 4) for s, t in stage_ms.items()},
+        "step_ms_events": {"p10": round(pc[10], 4), "median": round(pc[50], 4), "p90": round(pc[90], 4)},
         "fwd_tflops": round(fflops / (stage_ms["fwd"] * 1e-3) / 1e12, 2),
         "kernel_tflops": {s: round(kernel_flops(s, B, H, N, d, w.causal, sf) / (stage_ms[s] * 1e-3) / 1e12, 2)
                           for s in stages if s != "bwd_dot"},

@@ -89,3 +89,11 @@ def test_kvouter_bytes_grows_quadratically_and_causal_halves():
     assert 0.5 < c < 0.52
     # against the queries-outer floor: two orders of magnitude at N = 8192
     assert bench.kvouter_bytes(1, 16, 8192, 128, False) > 100 * bench.floor_bytes("fwd", 1, 16, 8192, 128)
+
+
+def test_step_percentiles_nearest_rank():
+    # nearest-rank on the sorted sample, whatever the input order
+    assert bench.percentiles([5.0, 1.0, 3.0, 2.0, 4.0]) == {10: 1.0, 50: 3.0, 90: 5.0}
+    xs = [float(i) for i in range(101)]
+    assert bench.percentiles(xs[::-1]) == {10: 10.0, 50: 50.0, 90: 90.0}
+    assert bench.percentiles([7.0]) == {10: 7.0, 50: 7.0, 90: 7.0}
