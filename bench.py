@@ -95,6 +95,32 @@ def floor_bytes(stage, B, H, N, d, elem=2) -> float:
     }[stage]
 
 
+def l2_read_model(stage, B, H, N, d, causal, block, elem=2) -> float:
+    """Bytes one launch reads from L2 under the blocked schedule, before any
+    L1 reuse: the operand that stays on chip is read once; the streamed pair
+    is read once per block of `block` rows that needs it (causal: only the
+    rows or keys on the block's side of the diagonal), plus the per-row fp32
+    statistics that come with it.
+      fwd       Q once; K, V per query block of `block` rows
+      bwd_dkdv  K, V once; Q, dO, LSE log2(e), D per key block of `block` keys
+      bwd_dq    Q, dO, LSE log2(e), D once; K, V per query block of `block` rows"""
+    nb = (N + block - 1) // block
+    if causal:
+        # query block i sees keys [0, (i+1) block); key block j is seen by rows [j block, N)
+        seen = sum(min(N, (i + 1) * block) for i in range(nb))
+        seen_t = sum(N - j * block for j in range(nb))
+    else:
+        seen = seen_t = nb * N
+    row = d * elem
+    if stage == "fwd":
+        return B * H * (N * row + 2 * seen * row)
+    if stage == "bwd_dkdv":
+        return B * H * (2 * N * row + seen_t * (2 * row + 8))
+    if stage == "bwd_dq":
+        return B * H * (N * (2 * row + 8) + 2 * seen * row)
+    raise ValueError(stage)
+
+
 def standard_io_elements(N, d) -> float:
     """Standard attention's HBM traffic in elements, 2N^2 + 4Nd, as the
     worked accounting of "01 · FlashAttention" (step 5 of 5, "show the
@@ -734,6 +760,14 @@ def digest(workload, stages, root=ROOT, steps=10, warmup=3):
     p1, p2, p3 = rows(1), rows(2), rows(3)
     cf, cw = copy_kib(p1, "FETCH_SIZE"), copy_kib(p2, "WRITE_SIZE")
     ff, fw = 512 * 1024 / cf, 512 * 1024 / cw
+    # optional fourth run: L2 read sectors (32 B), scaled by what the copy reads
+    p4_path = os.path.join(go, "pmc", f"{workload}_p4_counter_collection.csv")
+    p4 = rows(4) if os.path.exists(p4_path) else None
+    L2C = "TCC_READ_SECTORS_sum"
+    if p4 is not None:
+        cs = max((float(r["Counter_Value"]) for r in p4
+                  if r["Counter_Name"] == L2C and "copy" in r["Kernel_Name"].lower()), default=0.0)
+        fs = 512 * (1 << 20) / (32 * cs) if cs else 0.0
     for stage in stages:
         pats = DIGEST_PATTERNS[stage]
         fetch, kn = per_launch(p1, pats, "FETCH_SIZE")
@@ -746,9 +780,10 @@ def digest(workload, stages, root=ROOT, steps=10, warmup=3):
             floor = floor_bytes(stage, w.B, w.H, w.N, w.d)
         hbm = fetch * 1024 * ff + write * 1024 * fw
         what = "one launch" if len(kn) == 1 else f"one call (its {len(kn)} launches)"
+        groups = [(1, "FETCH_SIZE"), (2, "WRITE_SIZE"), (3, SQ_GROUP)] + ([(4, L2C)] if p4 is not None else [])
         cmd = [f"#   rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc -o {workload}_p{i} -- "
                f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --quick --copy-calibration 512"
-               for i, c in ((1, "FETCH_SIZE"), (2, "WRITE_SIZE"), (3, SQ_GROUP))]
+               for i, c in groups]
         busy = c3["SQ_BUSY_CU_CYCLES"]
         out = [f"# HBM traffic of {what} of the {stage} stage ({' + '.join(kn)}), {workload}",
                f"# ({wdesc}), from rocprofv3 counters.",
@@ -777,6 +812,19 @@ def digest(workload, stages, root=ROOT, steps=10, warmup=3):
                f"insts_lds: {c3['SQ_INSTS_LDS']:.4g}",
                f"lds_bank_conflict_cycles: {c3['SQ_LDS_BANK_CONFLICT']:.0f}",
                f"wait_inst_lds: {c3['SQ_WAIT_INST_LDS']:.4g}"]
+        if p4 is not None and fs:
+            sec, _ = per_launch(p4, pats, L2C)
+            l2 = sec * 32 * fs
+            out += ["# L2 read bytes: TCC_READ_SECTORS_sum (32-byte sectors) x 32, scaled by the same",
+                    f"# copy ({cs:.0f} sectors for 512 MiB read: factor {fs:.4f}).",
+                    f"l2_read_bytes_per_launch: {l2:.0f}"]
+            block = {"fwd": 256 if any("fwd_pp_kernel" in k for k in kn) else 128,
+                     "bwd_dkdv": 128, "bwd_dq": 128}.get(stage)
+            if block and not w.sparse_frac and not w.fp8:
+                model = l2_read_model(stage, w.B, w.H, w.N, w.d, w.causal, block)
+                out += [f"l2_read_model_bytes: {model:.0f}   # blocked schedule, {block}-row blocks "
+                        "(bench.l2_read_model)",
+                        f"l2_read_ratio_to_model: {l2/model:.3f}"]
         with open(os.path.join(root, "profiles", f"traffic_{stage}_{workload}.txt"), "w") as f:
             f.write("\n".join(out) + "\n")
         print("\n".join(out))

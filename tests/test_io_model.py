@@ -97,3 +97,21 @@ def test_step_percentiles_nearest_rank():
     xs = [float(i) for i in range(101)]
     assert bench.percentiles(xs[::-1]) == {10: 10.0, 50: 50.0, 90: 90.0}
     assert bench.percentiles([7.0]) == {10: 7.0, 50: 7.0, 90: 7.0}
+
+
+def test_l2_read_model_closed_forms():
+    B, H, N, d, blk = 2, 3, 1024, 64, 128
+    nb = N // blk
+    row = d * 2
+    # non-causal: the streamed pair is read once per block
+    assert bench.l2_read_model("fwd", B, H, N, d, False, blk) == B * H * (N * row + 2 * nb * N * row)
+    assert bench.l2_read_model("bwd_dq", B, H, N, d, False, blk) == B * H * (N * (2 * row + 8) + 2 * nb * N * row)
+    assert bench.l2_read_model("bwd_dkdv", B, H, N, d, False, blk) == B * H * (2 * N * row + nb * N * (2 * row + 8))
+    # causal: query block i sees (i + 1) blk keys; key block j is seen by N - j blk rows
+    seen = blk * nb * (nb + 1) // 2
+    seen_t = N * nb - blk * nb * (nb - 1) // 2
+    assert seen == seen_t      # the same triangle, counted from either side
+    assert bench.l2_read_model("fwd", B, H, N, d, True, blk) == B * H * (N * row + 2 * seen * row)
+    assert bench.l2_read_model("bwd_dkdv", B, H, N, d, True, blk) == B * H * (2 * N * row + seen_t * (2 * row + 8))
+    # one block covering everything: each operand read once, as the O(Nd) floor counts them
+    assert bench.l2_read_model("fwd", 1, 1, 256, 64, False, 256) == 3 * 256 * 64 * 2
