@@ -102,8 +102,12 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
     const int total = p.B * p.H * n_qblk;
     int bh, qb;
     if (CAUSAL) {
-        causal_item(blockIdx.x, p.B * p.H, n_qblk, l2_group(N, 4 * D), bh, qb);
-        qb = n_qblk - 1 - qb;                // rank 0 = the last block: longest rows
+        const int grp = l2_group(N, 4 * D);
+        causal_item(blockIdx.x, p.B * p.H, n_qblk, grp, bh, qb);
+        // rank 0 = the last block (longest rows), after the rotation that
+        // starts the ranks past the first round of workgroups first
+        const int rot = causal_rotation(p.B * p.H, n_qblk, grp, p.wg_slots);
+        qb = n_qblk - 1 - (qb + n_qblk - rot) % n_qblk;
     } else {
         const int w = xcd_remap(blockIdx.x, total);
         bh = w / n_qblk;
@@ -200,14 +204,18 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
         if (CAUSAL && kbase > wq0 + 31)
             return;
         if (decltype(masked)::value && ((kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0))) {
+            // register (kc, i) holds key kbase + 4 hf + o, o = 32 kc + 8 (i / 4) + i % 4: it is
+            // allowed iff o <= lim (below the key length and, causal, not after the query),
+            // one compare against a constant per score
+            int lim = kv_len - 1 - kbase - 4 * hf;
+            if (CAUSAL)
+                lim = min(lim, qrow - kbase - 4 * hf);
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kbase + kc * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
-                    if (key >= kv_len || (CAUSAL && key > qrow))
+                for (int i = 0; i < 16; ++i)
+                    if (kc * 32 + 8 * (i / 4) + (i % 4) > lim)
                         s[kc][i] = -INFINITY;
-                }
         }
         // Probabilities against the current reference m, with fp32 row sums
         // and bf16 operands for P V.  The reference must move (lazily: only
@@ -638,12 +646,28 @@ static hipError_t launch_t256_inst(const FwdArgs &a, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
+// workgroups of a kernel resident at once on one XCD (0 if unknown), queried
+// once per kernel: the number of CUs per XCD times the kernel's occupancy
+static int xcd_slots(const void *fn, int block)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess)
+        return 0;
+    return cus % 8 == 0 ? cus / 8 * per_cu : 0;
+}
+
 template <int D, int BC, bool CAUSAL, bool SPARSE>
 static hipError_t launch_bf16_inst(const FwdArgs &a, hipStream_t s)
 {
     const int n_qblk = (a.N + 127) / 128;
     const dim3 grid(a.B * a.H * n_qblk), block(256);
     FwdArgs args = a;
+    if constexpr (CAUSAL) {
+        static const int slots = xcd_slots((const void *)&fwd_bf16_kernel<D, BC, CAUSAL, SPARSE>, 256);
+        args.wg_slots = slots;
+    }
     float c = a.scale * kLog2e;
     void *kargs[] = {&args, &c};
     return hipLaunchKernel((const void *)&fwd_bf16_kernel<D, BC, CAUSAL, SPARSE>, grid, block,

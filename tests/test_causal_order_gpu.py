@@ -4,8 +4,10 @@ A causal grid hands its (head, row block) items to workgroups in one of three
 orders: heads of one XCD interleaved in groups sized to the XCD's L2 (the
 last group of an XCD may hold fewer heads), head by head when a head has
 fewer than four row blocks, and the plain XCD remap (or the identity) when
-the heads do not split evenly over the 8 XCDs.  Each shape below reaches one
-of them.  Every output element is prefilled with NaN, so an item that no
+the heads do not split evenly over the 8 XCDs.  In the forward, when one
+group holds all of an XCD's heads and its items overflow one round of
+resident workgroups, the ranks that would start last are started first.
+Each shape below reaches one of them.  Every output element is prefilled with NaN, so an item that no
 workgroup took shows up as a non-finite output; sampled rows of every head
 (and the backward on three heads) are compared with the fp64 oracle at the
 bf16 bars of the parity tests.
@@ -27,6 +29,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # (label, B, H, N, d)
     ("groups of 2 heads, last group of 1 (24 heads)", 1, 24, 8192, 64),
+    ("one group per XCD, ranks past the first round started first", 8, 16, 1024, 64),
     ("one group of 2 heads", 2, 8, 2048, 128),
     ("groups at head dim 256", 1, 16, 1024, 256),
     ("three row blocks per head: head by head", 2, 8, 384, 64),
