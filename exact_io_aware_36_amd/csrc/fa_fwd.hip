@@ -225,6 +225,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
         // partial row sum passes 2^TAU (or the row has no reference yet):
         // the common tile skips the max reduction.  Either way the result is
         // the one the max-first order gives.
+        // (the row sum starts at the first probability: an add to 0.0f is an
+        // instruction, kept for -0, which an exponential never is)
         float rs = 0.f;
         bf16x8 pb[NKC][2];
         bool slow = __any(m == -INFINITY);
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m));
-                    rs += pv;
+                    rs = (kc == 0 && i == 0) ? pv : rs + pv;
                     pb[kc][i / 8][i % 8] = (bf16)pv;
                 }
             slow = __any(!(rs <= kPassLimit));   // also catches inf
@@ -257,13 +259,12 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void fwd_bf16_kernel(FwdArgs
                     oacc[db] *= alpha;
             }
             const float m_use = (m == -INFINITY) ? 0.f : m;
-            rs = 0.f;
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m_use));
-                    rs += pv;
+                    rs = (kc == 0 && i == 0) ? pv : rs + pv;
                     pb[kc][i / 8][i % 8] = (bf16)pv;
                 }
         }

@@ -288,13 +288,19 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs p, float c_log2)
         float rs = 0.f;
         bool slow = __any(m == -INFINITY);
         if (!slow) {
-            float r4[4] = {0.f, 0.f, 0.f, 0.f};
+            // four partial sums, each started at its first probability (an add
+            // to 0.0f is an instruction: the compiler keeps it for -0, which an
+            // exponential never is)
+            float r4[4];
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m));
-                    r4[i % 4] += pv;
+                    if (kc == 0 && i < 4)
+                        r4[i] = pv;
+                    else
+                        r4[i % 4] += pv;
                     pb[kc][i / 8][i % 8] = (bf16)pv;
                 }
             rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
@@ -318,13 +324,19 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs p, float c_log2)
                     oacc[db] *= alpha;
             }
             const float m_use = (m == -INFINITY) ? 0.f : m;
-            float r4[4] = {0.f, 0.f, 0.f, 0.f};
+            // four partial sums, each started at its first probability (an add
+            // to 0.0f is an instruction: the compiler keeps it for -0, which an
+            // exponential never is)
+            float r4[4];
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float pv = exp2_hw(fmaf(s[kc][i], c_log2, -m_use));
-                    r4[i % 4] += pv;
+                    if (kc == 0 && i < 4)
+                        r4[i] = pv;
+                    else
+                        r4[i % 4] += pv;
                     pb[kc][i / 8][i % 8] = (bf16)pv;
                 }
             rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
