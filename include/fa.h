@@ -28,8 +28,11 @@
  *    j < kv_lens[b]; every query row is still computed and written.  A block
  *    mask excludes the keys of a zero block from the softmax entirely.
  *  - Pointers: every tensor pointer is a DEVICE pointer owned by the caller;
- *    outputs must not alias inputs.  The library allocates nothing, keeps no
- *    mutable global state and is re-entrant.
+ *    outputs must not alias inputs.  The library allocates nothing and is
+ *    re-entrant.  Its only global state: the fixed device array of
+ *    fa_bwd_noalloc (see there), and a per-kernel count of resident
+ *    workgroups that the first causal forward call queries and keeps (it
+ *    orders the causal work; results do not depend on it).
  *  - Streams: every call only enqueues work on `stream` (NULL = the default
  *    stream) and returns without synchronising; results are valid once the
  *    stream has reached that point.  Calls on different streams that share
