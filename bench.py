@@ -617,6 +617,127 @@ def metric_range(fa, torch, steps=5, warmup=2, ds=(64, 128)):
     return out
 
 
+def next_rows(fa, torch, workloads, steps=5, warmup=2):
+    """The extensions beyond the dense path, once each at their workloads'
+    shapes (timing only; parity is tested elsewhere): the block-sparse forward +
+    backward, the split-KV decode step, the d = 256 forward + backward and the
+    FP8 forward.  Q, K, V (and dO) are drawn on the GPU from a fixed seed at the
+    workload's input scale; key lengths and the block mask come from the
+    workload's own CPU generator.  Compute-bound rows give metric-convention
+    TFLOP/s against their MFMA peak, the decode step HBM GB/s against 8 TB/s."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    res = {}
+
+    def draw(w, shape, scale=None):
+        sc = w.input_scale if scale is None else scale
+        return (torch.randn(shape, generator=gen, device=dev) * sc).to(torch.bfloat16)
+
+    # block-sparse forward + backward
+    w = workloads.WORKLOADS["block_sparse_fwdbwd"]
+    gen.manual_seed(w.seed)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    q, k, v = (draw(w, (B, H, N, d)) for _ in range(3))
+    do = draw(w, (B, H, N, d), 1.0)
+    mask = workloads.block_mask(N // w.mask_block, w.sparse_frac,
+                                torch.Generator().manual_seed(w.seed)).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+
+    def sp_fwd():
+        fa.fa_fwd_blocksparse(q, k, v, o, lse, mask, mask_block=w.mask_block, scale=w.scale)
+
+    def sp_bwd():
+        fa.fa_bwd_blocksparse(q, k, v, o, do, lse, dq, dk, dv, ws, mask,
+                              mask_block=w.mask_block, scale=w.scale)
+
+    sp_fwd()
+    t_f = _timed(torch, stream, sp_fwd, warmup, steps)
+    t_b = _timed(torch, stream, sp_bwd, warmup, steps)
+    ff = fwd_flops(B, H, N, d, False, w.sparse_frac)
+    res["block_sparse_fwdbwd"] = {
+        "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+        "fwd_bwd_tflops": round(2.5 * ff / ((t_f + t_b) * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * 2.5 * ff / ((t_f + t_b) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2)}
+    del q, k, v, do, o, dq, dk, dv, ws
+
+    # split-KV decode step
+    w = workloads.WORKLOADS["decode_splitkv"]
+    gen.manual_seed(w.seed)
+    B, H, N, d, nq = w.B, w.H, w.N, w.d, w.nq
+    q = draw(w, (B, H, nq, d))
+    k, v = draw(w, (B, H, N, d)), draw(w, (B, H, N, d))
+    lo, hi = w.kv_len_range
+    lens_h = torch.randint(lo, hi + 1, (B,), generator=torch.Generator().manual_seed(w.seed),
+                           dtype=torch.int32)
+    lens = lens_h.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(fa.fa_fwd_splitkv_workspace_bytes(B, H, nq, N, d, 0), 256),
+                     dtype=torch.uint8, device=dev)
+
+    def dec():
+        fa.fa_fwd_splitkv(q, k, v, o, lse, ws, causal=w.causal, scale=w.scale, kv_lens=lens)
+
+    t = _timed(torch, stream, dec, warmup, steps)
+    _, nbytes = decode_accounting(B, H, nq, d, lens_h.tolist(), w.causal)
+    gbs = nbytes / (t * 1e-3) / 1e9
+    res["decode_splitkv"] = {"call_ms": round(t, 4), "hbm_gbs": round(gbs, 1),
+                             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+    del q, k, v, o, ws
+
+    # d = 256 forward + backward
+    w = workloads.WORKLOADS["d256_fwdbwd"]
+    gen.manual_seed(w.seed)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    q, k, v = (draw(w, (B, H, N, d)) for _ in range(3))
+    do = draw(w, (B, H, N, d), 1.0)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+
+    def f256():
+        fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale)
+
+    def b256():
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=w.causal, scale=w.scale)
+
+    f256()
+    t_f = _timed(torch, stream, f256, warmup, steps)
+    t_b = _timed(torch, stream, b256, warmup, steps)
+    ff = fwd_flops(B, H, N, d, w.causal)
+    res["d256_fwdbwd"] = {
+        "fwd_ms": round(t_f, 4), "fwd_tflops": round(ff / (t_f * 1e-3) / 1e12, 2),
+        "bwd_ms": round(t_b, 4),
+        "fwd_bwd_tflops": round(2.5 * ff / ((t_f + t_b) * 1e-3) / 1e12, 2)}
+    del q, k, v, do, o, dq, dk, dv, ws
+
+    # FP8 forward on quantised inputs (Q, K rotated with the workload's signs)
+    w = workloads.WORKLOADS["long_context_fp8"]
+    gen.manual_seed(w.seed)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    q, k, v = (draw(w, (B, H, N, d)) for _ in range(3))
+    signs = workloads.random_signs(d, w.seed).to(dev)
+    q8, qs = fa.quantize_fp8(q, 128, signs)
+    k8, ks = fa.quantize_fp8(k, 128, signs)
+    v8t, vs = fa.quantize_fp8(v, 0, None, transpose=True)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def f8():
+        fa.fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, o, lse, causal=w.causal, scale=w.scale)
+
+    t = _timed(torch, stream, f8, warmup, steps)
+    ff = fwd_flops(B, H, N, d, w.causal)
+    res["long_context_fp8"] = {"fwd_ms": round(t, 4), "fwd_tflops": round(ff / (t * 1e-3) / 1e12, 2),
+                               "pct_fp8_peak": round(100 * ff / (t * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 2)}
+    return res
+
+
 def other_configs(fa, torch, workloads, steps=10, warmup=3):
     """The other measured workloads once each (default kernels, their seeded
     inputs): the single-head fp32 forward, the GPT-2-shaped causal forward,
@@ -1026,6 +1147,7 @@ def main(argv=None):
     if not args.quick and args.workload == "long_context_causal":
         detail["sweep"] = metric_range(fa, torch)
         detail["configs"] = other_configs(fa, torch, workloads)
+        detail["next_rows"] = next_rows(fa, torch, workloads)
 
     cpu = None
     if not args.no_cpu_baseline:
