@@ -109,10 +109,10 @@ def oracle_inputs(inp, rot_seed=None):
     return q8, qs, k8, ks, v8, vs
 
 
-def run_fp8(fa, q8, qs, k8, ks, v8, vs, causal, lens):
+def run_fp8(fa, q8, qs, k8, ks, v8, vs, causal, lens, scale=None):
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     o, lse = fa.fwd_fp8(dev(q8), dev(k8), dev(v8.transpose(0, 1, 3, 2)), dev(qs), dev(ks),
-                        dev(vs.reshape(vs.shape[0], vs.shape[1])), causal=causal,
+                        dev(vs.reshape(vs.shape[0], vs.shape[1])), causal=causal, scale=scale,
                         kv_lens=None if lens is None else lens.cuda())
     torch.cuda.synchronize()
     return host(o), host(lse)

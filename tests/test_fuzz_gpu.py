@@ -102,16 +102,17 @@ def test_fuzz_blocksparse(fa, case):
     N = 128 * int(rng.integers(1, 6))        # the block-sparse entry points take N % 128 == 0
     nb = N // 128
     mask = (rng.random((nb, nb)) < rng.uniform(0.2, 0.9)).astype(np.uint8)
-    say(f"  sparse case {case}: H={H} N={N} d={d} mask rows {mask.sum(axis=1).tolist()}")
+    scale = float(rng.uniform(0.5, 1.5)) / math.sqrt(d)
+    say(f"  sparse case {case}: H={H} N={N} d={d} scale={scale:.4f} mask rows {mask.sum(axis=1).tolist()}")
     inp = workloads.random_qkv(B, H, N, d, seed=7400 + case)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "dout"))
     tm = torch.from_numpy(mask).cuda()
-    o, lse = fa.fwd_blocksparse(q, k, v, tm)
-    dq, dk, dv = fa.bwd_blocksparse(q, k, v, o, do, lse, tm)
+    o, lse = fa.fwd_blocksparse(q, k, v, tm, scale=scale)
+    dq, dk, dv = fa.bwd_blocksparse(q, k, v, o, do, lse, tm, scale=scale)
     torch.cuda.synchronize()
     Q, K, V, dO = f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["dout"])
-    O, L = oracle.fwd(Q, K, V, block_mask=mask)
-    dQ, dK, dV, _ = oracle.bwd(Q, K, V, dO, block_mask=mask)
+    O, L = oracle.fwd(Q, K, V, block_mask=mask, scale=scale)
+    dQ, dK, dV, _ = oracle.bwd(Q, K, V, dO, block_mask=mask, scale=scale)
     check_bf16("O", host(o), O)
     check_lse("LSE", host(lse), L)
     check_bf16("dQ", host(dq), dQ)
@@ -132,12 +133,13 @@ def test_fuzz_splitkv(fa, case):
     k = torch.randn((B, H, Nk, d), generator=gen).to(torch.bfloat16)
     v = torch.randn((B, H, Nk, d), generator=gen).to(torch.bfloat16)
     lens = workloads.random_lengths(B, 0, Nk, 7700 + case) if rng.integers(0, 2) else None
+    scale = float(rng.uniform(0.5, 1.5)) / math.sqrt(d)
     say(f"  decode case {case}: B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal} splits={ns} "
-        f"lens={None if lens is None else lens.tolist()}")
-    o, lse = fa.fwd_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal,
+        f"scale={scale:.4f} lens={None if lens is None else lens.tolist()}")
+    o, lse = fa.fwd_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale,
                             kv_lens=None if lens is None else lens.cuda(), num_splits=ns)
     torch.cuda.synchronize()
-    O, L = oracle.decode(f64(q), f64(k), f64(v), causal=causal, scale=1.0 / math.sqrt(d),
+    O, L = oracle.decode(f64(q), f64(k), f64(v), causal=causal, scale=scale,
                          kv_lens=None if lens is None else lens.numpy())
     check_bf16("O", host(o), O)
     check_lse("LSE", host(lse), L)
@@ -150,19 +152,22 @@ def test_fuzz_fp8_and_kvouter(fa, case):
     B, H = 1, int(rng.integers(1, 3))
     N = 16 * int(rng.integers(1, 40))
     causal = bool(rng.integers(0, 2))
-    say(f"  fp8 / keys-outer case {case}: H={H} N={N} d={d} causal={causal}")
+    scale = float(rng.uniform(0.5, 1.5)) / math.sqrt(d)
+    say(f"  fp8 / keys-outer case {case}: H={H} N={N} d={d} causal={causal} scale={scale:.4f}")
     inp = workloads.random_qkv(B, H, N, d, seed=7900 + case)
     signs = workloads.random_signs(d, 8000 + case).numpy()
     q8, qs = ofp8.quantize(inp["q"].float().numpy(), 128, signs)
     k8, ks = ofp8.quantize(inp["k"].float().numpy(), 128, signs)
     v8, vs = ofp8.quantize(inp["v"].float().numpy(), 0)
-    o8, l8 = run_fp8(fa, q8, qs, k8, ks, v8, vs, causal, None)
-    O8, L8, (Q8, K8, V8) = ofp8.reference(q8, k8, v8, qs, ks, vs, causal=causal, kv_lens=None)
-    check_bound("O fp8", o8, O8, ofp8.p_quant_bound(Q8, K8, V8, L8, causal=causal, kv_lens=None))
-    check_lse_bound("LSE fp8", l8, L8, ofp8.lse_bound(q8, qs, k8, ks, L8, causal=causal))
+    o8, l8 = run_fp8(fa, q8, qs, k8, ks, v8, vs, causal, None, scale=scale)
+    O8, L8, (Q8, K8, V8) = ofp8.reference(q8, k8, v8, qs, ks, vs, causal=causal, scale=scale,
+                                          kv_lens=None)
+    check_bound("O fp8", o8, O8, ofp8.p_quant_bound(Q8, K8, V8, L8, causal=causal, scale=scale,
+                                                    kv_lens=None))
+    check_lse_bound("LSE fp8", l8, L8, ofp8.lse_bound(q8, qs, k8, ks, L8, causal=causal, scale=scale))
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
-    o, lse = fa.fwd_kvouter(q, k, v, causal=causal)
+    o, lse = fa.fwd_kvouter(q, k, v, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    O, L = oracle.fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), causal=causal)
+    O, L = oracle.fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), causal=causal, scale=scale)
     check_bf16("O keys-outer", host(o), O)
     check_lse("LSE keys-outer", host(lse), L)
