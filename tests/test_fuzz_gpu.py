@@ -1,9 +1,11 @@
 """Seeded random configurations of every entry point against the fp64
 oracle, through the C ABI: shapes, head dimensions, masks, key lengths, key
-tiles and split counts drawn from one fixed seed per case, so a run is
-reproducible and names its case.  Same bars as the parity tests (bf16 O,
-dQ, dK, dV; LSE); the FP8 forward against the oracle's probability-rounding
-bound.  Sizes stay small enough for the oracle to finish in seconds.
+tiles, backward query tiles, softmax scales and split counts drawn from one
+fixed seed per case, so a run is reproducible and names its case.  Same bars
+as the parity tests (bf16 O, dQ, dK, dV; LSE; every fourth dense case also
+runs the fp32 forward on the same inputs at the fp32 bar); the FP8 forward
+against the oracle's probability-rounding bound.  Sizes stay small enough
+for the oracle to finish in seconds.
 
 The dense draws include key lengths as short as one key: then every query
 row of that batch puts its whole softmax on a handful of keys, and those
@@ -24,7 +26,8 @@ import oracle
 import oracle.fp8 as ofp8
 import workloads
 from test_fp8_gpu import check_bound, check_lse_bound, run_fp8
-from test_parity_gpu import BF16_MAX_ABS, BF16_REL_L2, check_bf16, check_lse, f64, half_ulp_bf16, host, say
+from test_parity_gpu import (BF16_MAX_ABS, BF16_REL_L2, FP32_MAX_ABS, check_bf16, check_lse, f64,
+                              half_ulp_bf16, host, say)
 from test_rescale_gpu import rounding_bounds
 
 pytestmark = pytest.mark.gpu
@@ -72,15 +75,17 @@ def test_fuzz_dense_fwd_bwd(fa, case):
     rng, B, H, N, d = draw(7000 + case)
     causal = bool(rng.integers(0, 2))
     padded = bool(rng.integers(0, 2))
-    tile = int(rng.choice([0, 32, 64] if d == 256 else [0, 64, 128]))
+    tile = int(rng.choice([0, 32, 64] if d == 256 else [0, 32, 64, 128, 256]))
     scale = float(rng.uniform(0.5, 1.5)) / math.sqrt(d)
     say(f"  dense case {case}: B={B} H={H} N={N} d={d} causal={causal} padded={padded} tile={tile} scale={scale:.4f}")
     inp = workloads.random_qkv(B, H, N, d, seed=7100 + case, input_scale=float(rng.uniform(0.3, 1.0)))
     lens = workloads.random_lengths(B, 1, N, 7200 + case) if padded else None
+    btile = int(rng.choice([0, 64, 128])) if d != 256 else 0
+    say(f"    backward query tile {btile}")
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "dout"))
     dl = None if lens is None else lens.cuda()
     o, lse = fa.fwd(q, k, v, causal=causal, scale=scale, kv_lens=dl, tile_n=tile)
-    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=causal, scale=scale, kv_lens=dl)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=causal, scale=scale, kv_lens=dl, tile_n=btile)
     torch.cuda.synchronize()
     ln = None if lens is None else lens.numpy()
     Q, K, V, dO = f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["dout"])
@@ -92,6 +97,14 @@ def test_fuzz_dense_fwd_bwd(fa, case):
     check_grad("dQ", host(dq), dQ, bq)
     check_grad("dK", host(dk), dK, bk)
     check_grad("dV", host(dv), dV, bv)
+    if d != 256 and case % 4 == 0:
+        # the fp32 forward on the same (exactly representable) inputs and scale
+        o32, lse32 = fa.fwd(q.float(), k.float(), v.float(), causal=causal, scale=scale, kv_lens=dl)
+        torch.cuda.synchronize()
+        d_o = float(np.abs(host(o32) - O).max())
+        say(f"    fp32 forward: O max_abs={d_o:.3e}")
+        assert d_o <= FP32_MAX_ABS
+        check_lse("LSE fp32", host(lse32), L, tol=FP32_MAX_ABS)
 
 
 @pytest.mark.parametrize("case", range(N_CASES // 2))
